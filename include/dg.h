@@ -1,0 +1,172 @@
+/*
+ * dg.h -- C ABI of the canvas denoising attention library (libdg.so, gfx950).
+ *
+ * The operations come from "DiffusionGemma Technical Report" (paperfeed.app
+ * summary page), section "The mechanism: an AR model turned inside out":
+ *   - a single transformer is run in two attention modes: the prompt and all
+ *     committed text are encoded causally into a KV cache, and a 256-token
+ *     canvas is refined with full bidirectional attention within itself while
+ *     cross-attending to that cache (dg_canvas_attn, dg_canvas_step_loop);
+ *   - once a canvas is fully denoised it is frozen, encoded causally and
+ *     appended to the cache, so the growing context is never re-encoded
+ *     (dg_commit_block).
+ * The same page (section "The numbers, honestly") and the report's abstract
+ * give the block size (256 positions) and the ~12 refinement passes per block
+ * that dg_canvas_step_loop is meant for.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Element type: DG_BF16 (bf16 storage, fp32 accumulation, bf16 output rounded
+ * to nearest-even) or DG_F32 (fp32 storage and arithmetic throughout).
+ *
+ * Layouts (all row-major, element strides implied by the shape):
+ *   queries q, q_blk, out ......... [B][Nc][Hq][D]
+ *   canvas / block K, V ........... [B][Nc][Hkv][D]     (dg_kv.capacity = Nc)
+ *   cache K, V .................... [B][capacity][Hkv][D]
+ * Query head h reads kv head h / (Hq / Hkv) (grouped-query attention with
+ * consecutive query heads sharing a kv head).  prefix_len[b] (host int32
+ * array of B entries) is the number of valid cache rows of sequence b.
+ *
+ * Ownership: the caller owns every buffer (inputs, outputs, cache, workspace)
+ * and keeps it alive until the work enqueued on `stream` has completed.  All
+ * device pointers must be 16-byte aligned.  The library allocates no device
+ * memory and keeps no state between calls.
+ *
+ * Streams and errors: `stream` is a hipStream_t passed as void* (NULL = the
+ * default stream).  Every argument is validated on the host before any HIP
+ * call; a rejected call enqueues nothing and returns a negative status.  DG_OK
+ * means the work was enqueued, not that it has finished.  Device faults surface
+ * at the caller's next synchronisation.  dg_last_error() gives a thread-local
+ * description of the last failure.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dg_status;
+
+enum {
+  DG_OK = 0,
+  DG_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  DG_ERR_SHAPE = -2,     /* unsupported or inconsistent shape                   */
+  DG_ERR_DTYPE = -3,     /* unknown element type                                */
+  DG_ERR_CAPACITY = -4,  /* prefix_len negative or beyond the cache capacity    */
+  DG_ERR_WORKSPACE = -5, /* workspace smaller than dg_workspace_bytes() asks    */
+  DG_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed          */
+  DG_ERR_ALIGN = -7      /* a device pointer is not 16-byte aligned             */
+};
+
+enum { DG_BF16 = 0, DG_F32 = 1 };
+
+/* Limits checked by every entry point. */
+#define DG_N_CANVAS 256  /* canvas / block length: fixed at 256 positions      */
+#define DG_MAX_BATCH 64  /* sequences per call                                  */
+
+typedef struct {
+  int32_t dtype;      /* DG_BF16 or DG_F32                                       */
+  int32_t batch;      /* B, 1..DG_MAX_BATCH                                      */
+  int32_t n_canvas;   /* Nc, must equal DG_N_CANVAS                              */
+  int32_t n_heads_q;  /* Hq >= 1, a multiple of n_heads_kv                       */
+  int32_t n_heads_kv; /* Hkv >= 1                                               */
+  int32_t head_dim;   /* D: 64 or 128                                           */
+  float scale;        /* softmax scale; <= 0 selects 1/sqrt(D)                   */
+} dg_shape;
+
+/* A pair of K and V buffers, each [B][capacity][Hkv][D]. */
+typedef struct {
+  void* k;
+  void* v;
+  int64_t capacity; /* rows per sequence (Nc for canvas/block buffers)           */
+} dg_kv;
+
+/*
+ * Workspace bytes that any call with this shape and every prefix_len[b] <=
+ * max_prefix_len needs (partial results of the split-key plan).  Returns 0 for
+ * an invalid shape.  Sizing once for the largest prefix a caller will reach
+ * makes one workspace serve a whole generation.
+ */
+size_t dg_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len);
+
+/*
+ * Canvas denoising step (bidirectional decoder of the mechanism section).
+ * For every sequence b, query head h and canvas row i:
+ *   out[b,i,h,:] = softmax_j(scale * <q[b,i,h,:], k_j>) v_j
+ * over j in { cache rows 0..prefix_len[b]-1 } U { canvas rows 0..Nc-1 } of kv
+ * head h / (Hq/Hkv); no mask.  The cache is only read.
+ *   q          [B][Nc][Hq][D] device
+ *   kv_cache   device cache (k, v, capacity), capacity >= prefix_len[b]
+ *   prefix_len host int32[B], 0 <= prefix_len[b] <= kv_cache->capacity
+ *   kv_canvas  device canvas K/V, capacity must equal Nc
+ *   out        [B][Nc][Hq][D] device, written completely
+ *   workspace  device scratch of ws_bytes >= dg_workspace_bytes(shape, max_b L_b)
+ *              (may be NULL when that is 0); contents are overwritten
+ */
+dg_status dg_canvas_attn(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
+                         const int32_t* prefix_len, const dg_kv* kv_canvas, void* out,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Block commit (causal encoder of the mechanism section).  Block row i of
+ * sequence b attends to cache rows 0..prefix_len[b]-1 and block rows 0..i
+ * (diagonal included):
+ *   out[b,i,h,:] = softmax_j(scale * <q_blk[b,i,h,:], k_j>) v_j
+ * and the block's K/V rows are written, bit for bit, into cache rows
+ * prefix_len[b] .. prefix_len[b]+Nc-1.  Cache rows below prefix_len[b] are not
+ * modified.  prefix_len itself is not changed: the caller advances it by Nc.
+ *   q_blk      [B][Nc][Hq][D] device
+ *   kv_blk     device block K/V, capacity must equal Nc
+ *   kv_cache   device cache; requires prefix_len[b] + Nc <= capacity
+ *   prefix_len host int32[B]
+ *   out        [B][Nc][Hq][D] device
+ *   workspace  as for dg_canvas_attn
+ */
+dg_status dg_commit_block(const dg_shape* shape, const void* q_blk, const dg_kv* kv_blk,
+                          const dg_kv* kv_cache, const int32_t* prefix_len, void* out,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * n_steps canvas steps against one fixed cache (the ~12 refinement passes of
+ * a block), enqueued in order on `stream`.  Step s reads
+ *   q + s*in_step_stride, kv_canvas->k + s*in_step_stride,
+ *   kv_canvas->v + s*in_step_stride
+ * and writes out + s*out_step_stride (strides in elements).  The result is bit
+ * for bit that of n_steps separate dg_canvas_attn calls: in the model, each
+ * step's queries depend on the previous step's output, so steps are never
+ * fused; the loop only removes per-call host work.  n_steps >= 0; the
+ * workspace is reused by every step.
+ */
+dg_status dg_canvas_step_loop(const dg_shape* shape, int32_t n_steps, const void* q,
+                              const dg_kv* kv_canvas, int64_t in_step_stride,
+                              const dg_kv* kv_cache, const int32_t* prefix_len, void* out,
+                              int64_t out_step_stride, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* dg_status_string(dg_status status);
+
+/* Thread-local description of the last failed call on this thread ("" if none). */
+const char* dg_last_error(void);
+
+/*
+ * Kernel timing for measurement.  While enabled, every attention kernel the
+ * library launches is bracketed by HIP events recorded on the launch stream.
+ * dg_kernel_timing_read() waits for the recorded events, returns the number of
+ * launches and the summed milliseconds of the split-key attention kernels
+ * (attn_ms) and of the merge kernels (merge_ms) since the last read, and
+ * clears the record.  At most 4096 launches are kept between reads; later ones
+ * are not timed.  Not thread-safe; for benchmarks only.
+ */
+dg_status dg_kernel_timing_enable(int32_t enable);
+dg_status dg_kernel_timing_read(int32_t* n_attn, double* attn_ms, int32_t* n_merge,
+                                double* merge_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */
