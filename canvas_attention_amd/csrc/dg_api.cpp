@@ -1,0 +1,369 @@
+// dg_api.cpp -- the C ABI of libdg: argument checks, the split-key plan and launches.
+//
+// Entry points follow the two attention modes of "DiffusionGemma Technical
+// Report" (paperfeed.app summary, section "The mechanism: an AR model turned
+// inside out"): the bidirectional canvas step over [cache ; canvas] and the
+// causal block commit that appends the block to the cache.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "dg.h"
+#include "dg_internal.h"
+
+namespace {
+
+using dg::AttnArgs;
+using dg::Plan;
+
+thread_local std::string g_last_error;
+
+dg_status fail(dg_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dg_status fail(dg_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elem_size(int dtype) { return dtype == DG_BF16 ? 2 : 4; }
+
+int rows_per_unit(int dtype) { return dtype == DG_BF16 ? dg::kRowsBf16 : dg::kRowsF32; }
+
+dg_status check_shape(const dg_shape* s) {
+  if (!s) return fail(DG_ERR_NULL, "shape is NULL");
+  if (s->dtype != DG_BF16 && s->dtype != DG_F32)
+    return fail(DG_ERR_DTYPE, "unknown dtype %d (DG_BF16=0, DG_F32=1)", s->dtype);
+  if (s->batch < 1 || s->batch > DG_MAX_BATCH)
+    return fail(DG_ERR_SHAPE, "batch %d outside 1..%d", s->batch, DG_MAX_BATCH);
+  if (s->n_canvas != DG_N_CANVAS)
+    return fail(DG_ERR_SHAPE, "n_canvas %d, must be %d", s->n_canvas, DG_N_CANVAS);
+  if (s->n_heads_kv < 1 || s->n_heads_q < 1 || s->n_heads_q > 1024)
+    return fail(DG_ERR_SHAPE, "head counts Hq=%d Hkv=%d invalid", s->n_heads_q, s->n_heads_kv);
+  if (s->n_heads_q % s->n_heads_kv != 0)
+    return fail(DG_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", s->n_heads_q, s->n_heads_kv);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(DG_ERR_SHAPE, "head_dim %d, must be 64 or 128", s->head_dim);
+  if (!(s->scale == s->scale) || isinf(s->scale))
+    return fail(DG_ERR_SHAPE, "scale is not finite");
+  return DG_OK;
+}
+
+float effective_scale(const dg_shape* s) {
+  return s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
+}
+
+// Keys per split forced through the environment (tests use it to exercise many
+// splits and ragged split ends); 0 when unset.
+int forced_split_keys() {
+  const char* e = getenv("DG_SPLIT_KEYS");
+  if (!e || !*e) return 0;
+  const long v = strtol(e, nullptr, 10);
+  if (v <= 0) return 0;
+  return (int)(((v + dg::kKeyGranule - 1) / dg::kKeyGranule) * dg::kKeyGranule);
+}
+
+// Target number of units: one workgroup per CU for the bf16 kernel (4 waves,
+// one per SIMD), one wave per SIMD for the fp32 kernel.
+int target_units(int dtype) { return device_cu_count() * (dtype == DG_BF16 ? 1 : 4); }
+
+// Split-key plan: every unit of every sequence gets about the same number of
+// keys, chosen so that the units fill the device about once.
+void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
+  const int R = rows_per_unit(s->dtype);
+  const int G = s->n_heads_q / s->n_heads_kv;
+  const int NRT = dg::kCanvas * G / R;
+  const int per_split = s->n_heads_kv * NRT;  // units per split index
+  int64_t W = 0;
+  for (int b = 0; b < s->batch; b++) W += (int64_t)(prefix_len[b] + dg::kCanvas) * per_split;
+  const int T = target_units(s->dtype);
+  int64_t kappa = (W + T - 1) / T;
+  kappa = ((kappa + dg::kKeyGranule - 1) / dg::kKeyGranule) * dg::kKeyGranule;
+  kappa = std::max<int64_t>(kappa, s->dtype == DG_BF16 ? 256 : 64);
+  const int forced = forced_split_keys();
+  if (forced) kappa = forced;
+  memset(p, 0, sizeof *p);
+  p->batch = s->batch;
+  p->n_rowtiles = NRT;
+  p->rows_per_unit = R;
+  int units = 0;
+  for (int b = 0; b < s->batch; b++) {
+    const int64_t K = (int64_t)prefix_len[b] + dg::kCanvas;
+    int S = (int)((K + kappa - 1) / kappa);
+    int64_t sk = (K + S - 1) / S;
+    sk = ((sk + dg::kKeyGranule - 1) / dg::kKeyGranule) * dg::kKeyGranule;
+    S = (int)((K + sk - 1) / sk);
+    p->seq[b].prefix_len = prefix_len[b];
+    p->seq[b].n_splits = S;
+    p->seq[b].split_keys = (int)sk;
+    p->seq[b].unit_base = units;
+    units += S * per_split;
+  }
+  p->n_units = units;
+}
+
+size_t plan_workspace(const dg_shape* s, const Plan& p) {
+  bool any = false;
+  for (int b = 0; b < p.batch; b++) any = any || p.seq[b].n_splits > 1;
+  if (!any) return 0;
+  return (size_t)p.n_units * p.rows_per_unit * (s->head_dim + 2) * sizeof(float);
+}
+
+// ------------------------------------------------------------ kernel timing
+constexpr int kMaxTimed = 4096;
+struct Timing {
+  bool enabled = false;
+  hipEvent_t ev[2][kMaxTimed][2];  // [attn/merge][launch][begin/end]
+  bool created[2][kMaxTimed] = {};
+  int count[2] = {0, 0};
+} g_timing;
+
+void time_begin(int kind, hipStream_t st) {
+  if (!g_timing.enabled) return;
+  const int k = g_timing.count[kind];
+  if (k >= kMaxTimed) return;
+  if (!g_timing.created[kind][k]) {
+    if (hipEventCreate(&g_timing.ev[kind][k][0]) != hipSuccess ||
+        hipEventCreate(&g_timing.ev[kind][k][1]) != hipSuccess)
+      return;
+    g_timing.created[kind][k] = true;
+  }
+  hipEventRecord(g_timing.ev[kind][k][0], st);
+}
+
+void time_end(int kind, hipStream_t st) {
+  if (!g_timing.enabled) return;
+  const int k = g_timing.count[kind];
+  if (k >= kMaxTimed || !g_timing.created[kind][k]) return;
+  hipEventRecord(g_timing.ev[kind][k][1], st);
+  g_timing.count[kind] = k + 1;
+}
+
+struct Call {
+  dg_shape shape;
+  Plan plan;
+  AttnArgs args;
+  bool causal;
+};
+
+dg_status prepare(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
+                  const int32_t* prefix_len, const dg_kv* kv_new, void* out, void* workspace,
+                  size_t ws_bytes, bool commit, Call* c) {
+  dg_status st = check_shape(shape);
+  if (st) return st;
+  if (!q || !out || !kv_cache || !kv_new || !prefix_len)
+    return fail(DG_ERR_NULL, "a required argument is NULL (q, out, caches or prefix_len)");
+  if (!kv_new->k || !kv_new->v) return fail(DG_ERR_NULL, "canvas/block K or V is NULL");
+  if (kv_new->capacity != DG_N_CANVAS)
+    return fail(DG_ERR_SHAPE, "canvas/block capacity %lld, must be %d",
+                (long long)kv_new->capacity, DG_N_CANVAS);
+  if (kv_cache->capacity < 0) return fail(DG_ERR_CAPACITY, "negative cache capacity");
+  if ((!kv_cache->k || !kv_cache->v) && (kv_cache->capacity > 0 || commit))
+    return fail(DG_ERR_NULL, "cache K or V is NULL");
+  const void* ptrs[] = {q, out, kv_new->k, kv_new->v, kv_cache->k, kv_cache->v, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(DG_ERR_ALIGN, "device pointer %p is not 16-byte aligned", p);
+  for (int b = 0; b < shape->batch; b++) {
+    const int64_t L = prefix_len[b];
+    if (L < 0) return fail(DG_ERR_CAPACITY, "prefix_len[%d] = %lld is negative", b, (long long)L);
+    const int64_t need = commit ? L + DG_N_CANVAS : L;
+    if (need > kv_cache->capacity)
+      return fail(DG_ERR_CAPACITY, "prefix_len[%d] = %lld%s exceeds cache capacity %lld", b,
+                  (long long)L, commit ? " + 256" : "", (long long)kv_cache->capacity);
+    if (L + DG_N_CANVAS > INT32_MAX / 2)
+      return fail(DG_ERR_CAPACITY, "prefix_len[%d] too large", b);
+  }
+  c->shape = *shape;
+  c->causal = commit;
+  make_plan(shape, prefix_len, &c->plan);
+  const size_t need_ws = plan_workspace(shape, c->plan);
+  if (need_ws > ws_bytes)
+    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes, this call needs %zu", ws_bytes, need_ws);
+  if (need_ws > 0 && !workspace) return fail(DG_ERR_NULL, "workspace is NULL");
+  AttnArgs& a = c->args;
+  a.q = q;
+  a.k_cache = kv_cache->k;
+  a.v_cache = kv_cache->v;
+  a.k_new = kv_new->k;
+  a.v_new = kv_new->v;
+  a.k_append = commit ? kv_cache->k : nullptr;
+  a.v_append = commit ? kv_cache->v : nullptr;
+  a.out = out;
+  a.part_o = (float*)workspace;
+  a.part_ml = workspace ? (float*)((char*)workspace + (size_t)c->plan.n_units *
+                                                           c->plan.rows_per_unit *
+                                                           shape->head_dim * sizeof(float))
+                        : nullptr;
+  a.cap = kv_cache->capacity;
+  a.n_heads_q = shape->n_heads_q;
+  a.n_heads_kv = shape->n_heads_kv;
+  a.scale_log2 = effective_scale(shape) * 1.4426950408889634f;
+  return DG_OK;
+}
+
+dg_status launch(const Call& c, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf16 = c.shape.dtype == DG_BF16;
+  time_begin(0, st);
+  int err = bf16 ? dg::launch_attn_bf16(c.args, c.plan, c.shape.head_dim, c.causal, stream)
+                 : dg::launch_attn_f32(c.args, c.plan, c.shape.head_dim, c.causal, stream);
+  time_end(0, st);
+  if (err != 0)
+    return fail(DG_ERR_HIP, "attention kernel launch failed: %s",
+                hipGetErrorString((hipError_t)err));
+  bool any = false;
+  for (int b = 0; b < c.plan.batch; b++) any = any || c.plan.seq[b].n_splits > 1;
+  if (any) {
+    time_begin(1, st);
+    err = dg::launch_merge(c.args, c.plan, c.shape.head_dim, bf16, stream);
+    time_end(1, st);
+    if (err != 0)
+      return fail(DG_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString((hipError_t)err));
+  }
+  if (getenv("DG_LOG")) {
+    fprintf(stderr, "[dg] %s units=%d R=%d NRT=%d", c.causal ? "commit" : "canvas",
+            c.plan.n_units, c.plan.rows_per_unit, c.plan.n_rowtiles);
+    for (int b = 0; b < c.plan.batch; b++)
+      fprintf(stderr, " | b%d L=%d S=%d keys/split=%d", b, c.plan.seq[b].prefix_len,
+              c.plan.seq[b].n_splits, c.plan.seq[b].split_keys);
+    fprintf(stderr, "\n");
+  }
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dg_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len) {
+  if (check_shape(shape) != DG_OK || max_prefix_len < 0 || max_prefix_len > INT32_MAX / 2)
+    return 0;
+  const int R = rows_per_unit(shape->dtype);
+  const int G = shape->n_heads_q / shape->n_heads_kv;
+  const int NRT = dg::kCanvas * G / R;
+  // The natural plan never exceeds T + B*Hkv*NRT units whatever the prefixes.
+  int64_t units = (int64_t)target_units(shape->dtype) + (int64_t)shape->batch * shape->n_heads_kv * NRT;
+  const int forced = forced_split_keys();
+  if (forced) {
+    const int64_t S = (max_prefix_len + dg::kCanvas + forced - 1) / forced;
+    units = std::max<int64_t>(units, S * shape->batch * shape->n_heads_kv * NRT);
+  }
+  return (size_t)units * R * (shape->head_dim + 2) * sizeof(float);
+}
+
+dg_status dg_canvas_attn(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
+                         const int32_t* prefix_len, const dg_kv* kv_canvas, void* out,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  Call c;
+  dg_status st = prepare(shape, q, kv_cache, prefix_len, kv_canvas, out, workspace, ws_bytes,
+                         false, &c);
+  if (st) return st;
+  return launch(c, stream);
+}
+
+dg_status dg_commit_block(const dg_shape* shape, const void* q_blk, const dg_kv* kv_blk,
+                          const dg_kv* kv_cache, const int32_t* prefix_len, void* out,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  Call c;
+  dg_status st = prepare(shape, q_blk, kv_cache, prefix_len, kv_blk, out, workspace, ws_bytes,
+                         true, &c);
+  if (st) return st;
+  return launch(c, stream);
+}
+
+dg_status dg_canvas_step_loop(const dg_shape* shape, int32_t n_steps, const void* q,
+                              int64_t q_step_stride, const dg_kv* kv_canvas,
+                              int64_t kv_step_stride, const dg_kv* kv_cache,
+                              const int32_t* prefix_len, void* out, int64_t out_step_stride,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  if (n_steps < 0) return fail(DG_ERR_SHAPE, "n_steps %d is negative", n_steps);
+  Call c;
+  dg_status st = prepare(shape, q, kv_cache, prefix_len, kv_canvas, out, workspace, ws_bytes,
+                         false, &c);
+  if (st) return st;
+  const size_t es = elem_size(shape->dtype);
+  if (((q_step_stride * (int64_t)es) & 15) || ((kv_step_stride * (int64_t)es) & 15) ||
+      ((out_step_stride * (int64_t)es) & 15))
+    return fail(DG_ERR_ALIGN, "step strides must keep 16-byte alignment");
+  for (int s = 0; s < n_steps; s++) {
+    Call cs = c;
+    cs.args.q = (const char*)q + (int64_t)s * q_step_stride * es;
+    cs.args.k_new = (const char*)kv_canvas->k + (int64_t)s * kv_step_stride * es;
+    cs.args.v_new = (const char*)kv_canvas->v + (int64_t)s * kv_step_stride * es;
+    cs.args.out = (char*)out + (int64_t)s * out_step_stride * es;
+    st = launch(cs, stream);
+    if (st) return st;
+  }
+  return DG_OK;
+}
+
+const char* dg_status_string(dg_status status) {
+  switch (status) {
+    case DG_OK: return "DG_OK";
+    case DG_ERR_NULL: return "DG_ERR_NULL";
+    case DG_ERR_SHAPE: return "DG_ERR_SHAPE";
+    case DG_ERR_DTYPE: return "DG_ERR_DTYPE";
+    case DG_ERR_CAPACITY: return "DG_ERR_CAPACITY";
+    case DG_ERR_WORKSPACE: return "DG_ERR_WORKSPACE";
+    case DG_ERR_HIP: return "DG_ERR_HIP";
+    case DG_ERR_ALIGN: return "DG_ERR_ALIGN";
+    default: return "DG_ERR_UNKNOWN";
+  }
+}
+
+const char* dg_last_error(void) { return g_last_error.c_str(); }
+
+dg_status dg_kernel_timing_enable(int32_t enable) {
+  g_timing.enabled = enable != 0;
+  return DG_OK;
+}
+
+dg_status dg_kernel_timing_read(int32_t* n_attn, double* attn_ms, int32_t* n_merge,
+                                double* merge_ms) {
+  double tot[2] = {0, 0};
+  for (int kind = 0; kind < 2; kind++) {
+    for (int k = 0; k < g_timing.count[kind]; k++) {
+      if (hipEventSynchronize(g_timing.ev[kind][k][1]) != hipSuccess)
+        return fail(DG_ERR_HIP, "hipEventSynchronize failed");
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, g_timing.ev[kind][k][0], g_timing.ev[kind][k][1]) !=
+          hipSuccess)
+        return fail(DG_ERR_HIP, "hipEventElapsedTime failed");
+      tot[kind] += ms;
+    }
+  }
+  if (n_attn) *n_attn = g_timing.count[0];
+  if (n_merge) *n_merge = g_timing.count[1];
+  if (attn_ms) *attn_ms = tot[0];
+  if (merge_ms) *merge_ms = tot[1];
+  g_timing.count[0] = g_timing.count[1] = 0;
+  return DG_OK;
+}
+
+}  // extern "C"

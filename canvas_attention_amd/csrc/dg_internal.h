@@ -1,0 +1,66 @@
+// dg_internal.h -- types shared by the host API and the gfx950 kernels of libdg.
+//
+// Work decomposition ("split-key plan").  For every sequence b the key space
+// of one call is the concatenation [cache rows 0..L_b-1 ; canvas or block rows
+// 0..255].  Query rows of one kv head are packed: packed row p = i*G + hh is
+// canvas row i of query head g*G + hh, so the G query heads sharing kv head g
+// form one matrix of 256*G rows.  A work unit is (sequence b, kv head g, key
+// split s, row tile rt): rows [rt*R, rt*R+R) of that packed matrix against keys
+// [s*split_keys, min((s+1)*split_keys, end)).  Each unit writes one partial
+// result (normalised output rows plus log2-domain max and sum) that a merge
+// kernel combines; a sequence with a single split writes its output directly.
+#pragma once
+#include <stdint.h>
+
+#include "dg.h"
+
+namespace dg {
+
+constexpr int kCanvas = DG_N_CANVAS;
+constexpr int kMaxBatch = DG_MAX_BATCH;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
+
+struct SeqPlan {
+  int32_t prefix_len;  // L_b
+  int32_t n_splits;    // S_b >= 1
+  int32_t split_keys;  // keys per split (multiple of 32); the last split may be shorter
+  int32_t unit_base;   // first logical unit index of this sequence
+};
+
+struct Plan {
+  int32_t batch;
+  int32_t n_units;      // total logical units = grid size of the attention kernel
+  int32_t n_rowtiles;   // NRT = 256*G / R
+  int32_t rows_per_unit;// R
+  SeqPlan seq[kMaxBatch];
+};
+
+struct AttnArgs {
+  const void* q;        // [B][256][Hq][D]
+  const void* k_cache;  // [B][cap][Hkv][D]
+  const void* v_cache;
+  const void* k_new;    // canvas (step) or block (commit) K/V [B][256][Hkv][D]
+  const void* v_new;
+  void* k_append;       // commit only: cache K/V written at rows L..L+255 (else null)
+  void* v_append;
+  void* out;            // [B][256][Hq][D]
+  float* part_o;        // [n_units][R][D] normalised partial outputs
+  float* part_ml;       // [n_units][R][2]: max (log2 domain) and sum
+  int64_t cap;
+  int32_t n_heads_q;
+  int32_t n_heads_kv;
+  float scale_log2;     // softmax scale * log2(e)
+};
+
+// Host-side launchers (defined next to their kernels).  Each returns the HIP
+// error of the launch.
+int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream);
+int launch_attn_f32(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream);
+int launch_merge(const AttnArgs& a, const Plan& p, int head_dim, bool bf16_out, void* stream);
+
+// Rows per unit and key granule of each kernel family.
+constexpr int kRowsBf16 = 256;
+constexpr int kRowsF32 = 64;
+constexpr int kKeyGranule = 32;
+
+}  // namespace dg

@@ -1,0 +1,230 @@
+"""Thin Python binding of libdg.so (the gfx950 canvas-attention library).
+
+Argument marshalling only: every tensor is passed to the C ABI in
+include/dg.h as ``data_ptr()`` plus the current HIP stream; all of the
+arithmetic runs in the library's kernels.  torch provides device memory and
+streams.  Importing this module raises if libdg.so has not been built -- there
+is no CPU fallback.
+
+Functions mirror the C entry points: ``canvas_attn``, ``commit_block``,
+``canvas_step_loop``, ``workspace_bytes``, ``kernel_timing_enable`` and
+``kernel_timing_read``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg.so")
+
+DG_BF16, DG_F32 = 0, 1
+N_CANVAS = 256
+STATUS = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_DTYPE",
+          -4: "DG_ERR_CAPACITY", -5: "DG_ERR_WORKSPACE", -6: "DG_ERR_HIP", -7: "DG_ERR_ALIGN"}
+
+
+class DgShape(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("n_canvas", ctypes.c_int32), ("n_heads_q", ctypes.c_int32),
+                ("n_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class DgKv(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
+
+
+class DgError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}: {detail}")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m canvas_attention_amd.build` "
+                      "(there is no CPU fallback for the GPU path)")
+
+lib = ctypes.CDLL(LIB_PATH)
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_P = ctypes.POINTER
+lib.dg_workspace_bytes.argtypes = [_P(DgShape), _i64]
+lib.dg_workspace_bytes.restype = _sz
+lib.dg_canvas_attn.argtypes = [_P(DgShape), _vp, _P(DgKv), _vp, _P(DgKv), _vp, _vp, _sz, _vp]
+lib.dg_canvas_attn.restype = _i32
+lib.dg_commit_block.argtypes = [_P(DgShape), _vp, _P(DgKv), _P(DgKv), _vp, _vp, _vp, _sz, _vp]
+lib.dg_commit_block.restype = _i32
+lib.dg_canvas_step_loop.argtypes = [_P(DgShape), _i32, _vp, _i64, _P(DgKv), _i64, _P(DgKv), _vp,
+                                    _vp, _i64, _vp, _sz, _vp]
+lib.dg_canvas_step_loop.restype = _i32
+lib.dg_status_string.argtypes = [_i32]
+lib.dg_status_string.restype = ctypes.c_char_p
+lib.dg_last_error.argtypes = []
+lib.dg_last_error.restype = ctypes.c_char_p
+lib.dg_kernel_timing_enable.argtypes = [_i32]
+lib.dg_kernel_timing_enable.restype = _i32
+lib.dg_kernel_timing_read.argtypes = [_P(_i32), _P(ctypes.c_double), _P(_i32),
+                                      _P(ctypes.c_double)]
+lib.dg_kernel_timing_read.restype = _i32
+
+EXPORTS = ["dg_workspace_bytes", "dg_canvas_attn", "dg_commit_block", "dg_canvas_step_loop",
+           "dg_status_string", "dg_last_error", "dg_kernel_timing_enable",
+           "dg_kernel_timing_read"]
+
+
+def _check(fn, status):
+    if status != 0:
+        raise DgError(fn, status, lib.dg_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DG_BF16
+    if t.dtype == torch.float32:
+        return DG_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; bfloat16 or float32")
+
+
+def _shape(q: torch.Tensor, hkv: int, scale) -> DgShape:
+    B, Nc, Hq, D = q.shape
+    return DgShape(_dtype_code(q), B, Nc, Hq, hkv, D, float(scale) if scale else 0.0)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t: torch.Tensor, name: str, dtype, dims: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.dim() != dims or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dims}-d tensor")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _prefix(prefix_len, batch):
+    arr = (ctypes.c_int32 * batch)(*[int(x) for x in prefix_len])
+    if len(prefix_len) != batch:
+        raise ValueError(f"prefix_len has {len(prefix_len)} entries, batch is {batch}")
+    return arr
+
+
+def workspace_bytes(batch, n_heads_q, n_heads_kv, head_dim, max_prefix_len,
+                    dtype=torch.bfloat16) -> int:
+    """Bytes of workspace any call of this shape needs (see dg_workspace_bytes)."""
+    code = DG_BF16 if dtype == torch.bfloat16 else DG_F32
+    shape = DgShape(code, batch, N_CANVAS, n_heads_q, n_heads_kv, head_dim, 0.0)
+    n = lib.dg_workspace_bytes(ctypes.byref(shape), int(max_prefix_len))
+    if n == 0:
+        # zero is also the answer for a valid shape that needs no partials
+        pass
+    return int(n)
+
+
+def alloc_workspace(q: torch.Tensor, n_heads_kv: int, max_prefix_len: int) -> torch.Tensor:
+    B, _, Hq, D = q.shape
+    n = workspace_bytes(B, Hq, n_heads_kv, D, max_prefix_len, q.dtype)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+
+
+def canvas_attn(q, k_cache, v_cache, prefix_len, k_canvas, v_canvas, out=None, workspace=None,
+                scale=None, stream=None):
+    """dg_canvas_attn: q [B,256,Hq,D]; caches [B,cap,Hkv,D]; canvas K/V [B,256,Hkv,D]."""
+    dt = q.dtype
+    _need(q, "q", dt, 4)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_canvas", k_canvas),
+                    ("v_canvas", v_canvas)):
+        _need(t, name, dt, 4)
+    hkv = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dt, 4)
+    if workspace is None:
+        workspace = alloc_workspace(q, hkv, max(int(x) for x in prefix_len))
+    shape = _shape(q, hkv, scale)
+    cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])
+    canv = DgKv(k_canvas.data_ptr(), v_canvas.data_ptr(), k_canvas.shape[1])
+    st = lib.dg_canvas_attn(ctypes.byref(shape), _ptr(q), ctypes.byref(cache),
+                            _prefix(prefix_len, q.shape[0]), ctypes.byref(canv), _ptr(out),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream(stream))
+    _check("dg_canvas_attn", st)
+    return out
+
+
+def commit_block(q_blk, k_blk, v_blk, k_cache, v_cache, prefix_len, out=None, workspace=None,
+                 scale=None, stream=None):
+    """dg_commit_block: causal block attention, then block K/V appended to the cache."""
+    dt = q_blk.dtype
+    _need(q_blk, "q_blk", dt, 4)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_blk", k_blk),
+                    ("v_blk", v_blk)):
+        _need(t, name, dt, 4)
+    hkv = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q_blk)
+    _need(out, "out", dt, 4)
+    if workspace is None:
+        workspace = alloc_workspace(q_blk, hkv, max(int(x) for x in prefix_len))
+    shape = _shape(q_blk, hkv, scale)
+    blk = DgKv(k_blk.data_ptr(), v_blk.data_ptr(), k_blk.shape[1])
+    cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])
+    st = lib.dg_commit_block(ctypes.byref(shape), _ptr(q_blk), ctypes.byref(blk),
+                             ctypes.byref(cache), _prefix(prefix_len, q_blk.shape[0]),
+                             _ptr(out), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("dg_commit_block", st)
+    return out
+
+
+def canvas_step_loop(q_steps, k_steps, v_steps, k_cache, v_cache, prefix_len, out=None,
+                     workspace=None, scale=None, stream=None):
+    """dg_canvas_step_loop over N steps: q_steps [N,B,256,Hq,D], k/v_steps [N,B,256,Hkv,D]."""
+    dt = q_steps.dtype
+    _need(q_steps, "q_steps", dt, 5)
+    _need(k_steps, "k_steps", dt, 5)
+    _need(v_steps, "v_steps", dt, 5)
+    _need(k_cache, "k_cache", dt, 4)
+    _need(v_cache, "v_cache", dt, 4)
+    n = q_steps.shape[0]
+    hkv = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q_steps)
+    _need(out, "out", dt, 5)
+    q0 = q_steps[0]
+    if workspace is None:
+        workspace = alloc_workspace(q0, hkv, max(int(x) for x in prefix_len))
+    shape = _shape(q0, hkv, scale)
+    canv = DgKv(k_steps.data_ptr(), v_steps.data_ptr(), k_steps.shape[2])
+    cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])
+    st = lib.dg_canvas_step_loop(ctypes.byref(shape), n, _ptr(q_steps), q_steps[0].numel(),
+                                 ctypes.byref(canv), k_steps[0].numel(), ctypes.byref(cache),
+                                 _prefix(prefix_len, q0.shape[0]), _ptr(out), out[0].numel(),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    _check("dg_canvas_step_loop", st)
+    return out
+
+
+def kernel_timing_enable(on: bool = True):
+    _check("dg_kernel_timing_enable", lib.dg_kernel_timing_enable(1 if on else 0))
+
+
+def kernel_timing_read():
+    """(n_attn, attn_ms, n_merge, merge_ms) since the previous read."""
+    na, nm = ctypes.c_int32(), ctypes.c_int32()
+    ta, tm = ctypes.c_double(), ctypes.c_double()
+    _check("dg_kernel_timing_read", lib.dg_kernel_timing_read(ctypes.byref(na), ctypes.byref(ta),
+                                                              ctypes.byref(nm), ctypes.byref(tm)))
+    return na.value, ta.value, nm.value, tm.value

@@ -133,19 +133,20 @@ dg_status dg_commit_block(const dg_shape* shape, const void* q_blk, const dg_kv*
 /*
  * n_steps canvas steps against one fixed cache (the ~12 refinement passes of
  * a block), enqueued in order on `stream`.  Step s reads
- *   q + s*in_step_stride, kv_canvas->k + s*in_step_stride,
- *   kv_canvas->v + s*in_step_stride
- * and writes out + s*out_step_stride (strides in elements).  The result is bit
- * for bit that of n_steps separate dg_canvas_attn calls: in the model, each
- * step's queries depend on the previous step's output, so steps are never
- * fused; the loop only removes per-call host work.  n_steps >= 0; the
- * workspace is reused by every step.
+ *   q + s*q_step_stride, kv_canvas->k + s*kv_step_stride,
+ *   kv_canvas->v + s*kv_step_stride
+ * and writes out + s*out_step_stride (all strides in elements, each step laid
+ * out as for dg_canvas_attn).  The result is bit for bit that of n_steps
+ * separate dg_canvas_attn calls: in the model each step's queries depend on
+ * the previous step's output, so steps are never fused; the loop plans once
+ * and only removes per-call host work.  n_steps >= 0; the workspace is reused
+ * by every step.
  */
 dg_status dg_canvas_step_loop(const dg_shape* shape, int32_t n_steps, const void* q,
-                              const dg_kv* kv_canvas, int64_t in_step_stride,
-                              const dg_kv* kv_cache, const int32_t* prefix_len, void* out,
-                              int64_t out_step_stride, void* workspace, size_t ws_bytes,
-                              void* stream);
+                              int64_t q_step_stride, const dg_kv* kv_canvas,
+                              int64_t kv_step_stride, const dg_kv* kv_cache,
+                              const int32_t* prefix_len, void* out, int64_t out_step_stride,
+                              void* workspace, size_t ws_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* dg_status_string(dg_status status);

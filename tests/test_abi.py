@@ -1,0 +1,139 @@
+"""CPU-only checks of the C ABI: the library loads, exports every entry point
+declared in include/dg.h, and rejects bad arguments on the host before any HIP
+call (fake device pointers are never dereferenced on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+
+@pytest.fixture(scope="module")
+def dg():
+    from canvas_attention_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    import canvas_attention_amd.dg as dg_mod
+    return dg_mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for n in ("dg_canvas_attn", "dg_commit_block", "dg_canvas_step_loop", "dg_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(dg):
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(dg.lib, n), f"libdg.so does not export {n}"
+    assert set(dg.EXPORTS) == set(names)
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced by the rejected calls
+
+
+def shape(dg, **kw):
+    d = dict(dtype=0, batch=1, n_canvas=256, n_heads_q=16, n_heads_kv=8, head_dim=128, scale=0.0)
+    d.update(kw)
+    return dg.DgShape(**d)
+
+
+def call_canvas(dg, sh, q=FAKE, cache=None, prefix=(0,), canvas=None, out=FAKE, ws=FAKE,
+                ws_bytes=1 << 40):
+    cache = cache or dg.DgKv(FAKE, FAKE, 4096)
+    canvas = canvas or dg.DgKv(FAKE, FAKE, 256)
+    pl = (ctypes.c_int32 * len(prefix))(*prefix)
+    return dg.lib.dg_canvas_attn(ctypes.byref(sh), q, ctypes.byref(cache), pl,
+                                 ctypes.byref(canvas), out, ws, ws_bytes, None)
+
+
+def call_commit(dg, sh, cache=None, prefix=(0,), ws_bytes=1 << 40):
+    cache = cache or dg.DgKv(FAKE, FAKE, 4096)
+    blk = dg.DgKv(FAKE, FAKE, 256)
+    pl = (ctypes.c_int32 * len(prefix))(*prefix)
+    return dg.lib.dg_commit_block(ctypes.byref(sh), FAKE, ctypes.byref(blk), ctypes.byref(cache),
+                                  pl, FAKE, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), -3),
+    (dict(batch=0), -2),
+    (dict(batch=65), -2),
+    (dict(n_canvas=128), -2),
+    (dict(n_heads_q=12, n_heads_kv=8), -2),
+    (dict(head_dim=96), -2),
+    (dict(n_heads_kv=0), -2),
+    (dict(scale=float("nan")), -2),
+])
+def test_shape_errors(dg, kw, code):
+    st = call_canvas(dg, shape(dg, **kw), prefix=(0,) * max(1, kw.get("batch", 1) or 1))
+    assert st == code, (st, dg.lib.dg_last_error())
+    assert dg.lib.dg_last_error().decode()
+
+
+def test_null_and_alignment_errors(dg):
+    sh = shape(dg)
+    assert call_canvas(dg, sh, q=None) == -1
+    assert call_canvas(dg, sh, out=None) == -1
+    assert call_canvas(dg, sh, canvas=dg.DgKv(None, FAKE, 256)) == -1
+    assert call_canvas(dg, sh, cache=dg.DgKv(None, FAKE, 64)) == -1
+    assert call_canvas(dg, sh, q=FAKE + 8) == -7
+    assert call_canvas(dg, sh, cache=dg.DgKv(FAKE + 2, FAKE, 64)) == -7
+
+
+def test_capacity_errors(dg):
+    sh = shape(dg)
+    assert call_canvas(dg, sh, prefix=(-1,)) == -4
+    assert call_canvas(dg, sh, cache=dg.DgKv(FAKE, FAKE, 100), prefix=(101,)) == -4
+    assert call_canvas(dg, sh, canvas=dg.DgKv(FAKE, FAKE, 255)) == -2
+    # commit needs room for the whole block behind the prefix
+    assert call_commit(dg, sh, cache=dg.DgKv(FAKE, FAKE, 300), prefix=(45,)) == -4
+    assert "exceeds cache capacity" in dg.lib.dg_last_error().decode()
+    # a commit may never run on a cache without storage
+    assert call_commit(dg, sh, cache=dg.DgKv(None, None, 0), prefix=(0,)) in (-1, -4)
+
+
+def test_workspace_too_small(dg):
+    sh = shape(dg)
+    st = call_canvas(dg, sh, prefix=(4000,), ws_bytes=1024)
+    assert st == -5
+    assert "workspace" in dg.lib.dg_last_error().decode()
+
+
+def test_step_loop_errors(dg):
+    sh = shape(dg)
+    cache = dg.DgKv(FAKE, FAKE, 4096)
+    canv = dg.DgKv(FAKE, FAKE, 256)
+    pl = (ctypes.c_int32 * 1)(0)
+    st = dg.lib.dg_canvas_step_loop(ctypes.byref(sh), -1, FAKE, 0, ctypes.byref(canv), 0,
+                                    ctypes.byref(cache), pl, FAKE, 0, FAKE, 1 << 40, None)
+    assert st == -2
+    st = dg.lib.dg_canvas_step_loop(ctypes.byref(sh), 2, FAKE, 3, ctypes.byref(canv), 0,
+                                    ctypes.byref(cache), pl, FAKE, 0, FAKE, 1 << 40, None)
+    assert st == -7
+
+
+def test_workspace_bytes(dg):
+    assert dg.lib.dg_workspace_bytes(ctypes.byref(shape(dg, head_dim=96)), 1000) == 0
+    assert dg.lib.dg_workspace_bytes(ctypes.byref(shape(dg)), -1) == 0
+    n = dg.lib.dg_workspace_bytes(ctypes.byref(shape(dg)), 8192)
+    assert n > 0 and n % 4 == 0
+    n32 = dg.lib.dg_workspace_bytes(ctypes.byref(shape(dg, dtype=1, head_dim=64)), 64)
+    assert n32 > 0
+
+
+def test_status_strings(dg):
+    for code, name in dg.STATUS.items():
+        assert dg.lib.dg_status_string(code).decode() == name
+    assert dg.lib.dg_status_string(-99).decode() == "DG_ERR_UNKNOWN"
