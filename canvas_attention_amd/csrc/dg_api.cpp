@@ -54,7 +54,21 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t elem_size(int dtype) { return dtype == DG_BF16 ? 2 : 4; }
 
-int rows_per_unit(int dtype) { return dtype == DG_BF16 ? dg::kRowsBf16 : dg::kRowsF32; }
+// bf16 kernel shape for a call: DG_VARIANT=0..2 forces one for head_dim 128
+// (for tuning); otherwise the default shape.  head_dim 64 has one shape.
+int bf16_variant(int head_dim) {
+  if (head_dim != 128) return dg::kDefaultVariant;
+  const char* e = getenv("DG_VARIANT");
+  if (e && *e) {
+    const long v = strtol(e, nullptr, 10);
+    if (v >= 0 && v < dg::kNumVariants) return (int)v;
+  }
+  return dg::kDefaultVariant;
+}
+
+int rows_per_unit(int dtype, int variant) {
+  return dtype == DG_BF16 ? dg::variant_rows(variant) : dg::kRowsF32;
+}
 
 dg_status check_shape(const dg_shape* s) {
   if (!s) return fail(DG_ERR_NULL, "shape is NULL");
@@ -96,7 +110,8 @@ int target_units(int dtype) { return device_cu_count() * (dtype == DG_BF16 ? 1 :
 // Split-key plan: every unit of every sequence gets about the same number of
 // keys, chosen so that the units fill the device about once.
 void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
-  const int R = rows_per_unit(s->dtype);
+  const int variant = bf16_variant(s->head_dim);
+  const int R = rows_per_unit(s->dtype, variant);
   const int G = s->n_heads_q / s->n_heads_kv;
   const int NRT = dg::kCanvas * G / R;
   const int per_split = s->n_heads_kv * NRT;  // units per split index
@@ -110,6 +125,7 @@ void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
   if (forced) kappa = forced;
   memset(p, 0, sizeof *p);
   p->batch = s->batch;
+  p->variant = variant;
   p->n_rowtiles = NRT;
   p->rows_per_unit = R;
   int units = 0;
@@ -128,11 +144,16 @@ void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
   p->n_units = units;
 }
 
+// Bytes of one partial row: the normalised output (bf16 or fp32) plus max and sum.
+size_t partial_row_bytes(const dg_shape* s) {
+  return (size_t)s->head_dim * elem_size(s->dtype) + 2 * sizeof(float);
+}
+
 size_t plan_workspace(const dg_shape* s, const Plan& p) {
   bool any = false;
   for (int b = 0; b < p.batch; b++) any = any || p.seq[b].n_splits > 1;
   if (!any) return 0;
-  return (size_t)p.n_units * p.rows_per_unit * (s->head_dim + 2) * sizeof(float);
+  return (size_t)p.n_units * p.rows_per_unit * partial_row_bytes(s);
 }
 
 // ------------------------------------------------------------ kernel timing
@@ -215,10 +236,10 @@ dg_status prepare(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
   a.k_append = commit ? kv_cache->k : nullptr;
   a.v_append = commit ? kv_cache->v : nullptr;
   a.out = out;
-  a.part_o = (float*)workspace;
+  a.part_o = workspace;
   a.part_ml = workspace ? (float*)((char*)workspace + (size_t)c->plan.n_units *
                                                            c->plan.rows_per_unit *
-                                                           shape->head_dim * sizeof(float))
+                                                           shape->head_dim * elem_size(shape->dtype))
                         : nullptr;
   a.cap = kv_cache->capacity;
   a.n_heads_q = shape->n_heads_q;
@@ -247,8 +268,8 @@ dg_status launch(const Call& c, void* stream) {
       return fail(DG_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString((hipError_t)err));
   }
   if (getenv("DG_LOG")) {
-    fprintf(stderr, "[dg] %s units=%d R=%d NRT=%d", c.causal ? "commit" : "canvas",
-            c.plan.n_units, c.plan.rows_per_unit, c.plan.n_rowtiles);
+    fprintf(stderr, "[dg] %s variant=%d units=%d R=%d NRT=%d", c.causal ? "commit" : "canvas",
+            c.plan.variant, c.plan.n_units, c.plan.rows_per_unit, c.plan.n_rowtiles);
     for (int b = 0; b < c.plan.batch; b++)
       fprintf(stderr, " | b%d L=%d S=%d keys/split=%d", b, c.plan.seq[b].prefix_len,
               c.plan.seq[b].n_splits, c.plan.seq[b].split_keys);
@@ -264,17 +285,18 @@ extern "C" {
 size_t dg_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len) {
   if (check_shape(shape) != DG_OK || max_prefix_len < 0 || max_prefix_len > INT32_MAX / 2)
     return 0;
-  const int R = rows_per_unit(shape->dtype);
+  // The natural plan never exceeds T + B*Hkv*NRT units whatever the prefixes;
+  // the bound in bytes is largest for the widest row tile.
+  const int R = shape->dtype == DG_BF16 ? dg::variant_rows(dg::kVariantR256) : dg::kRowsF32;
   const int G = shape->n_heads_q / shape->n_heads_kv;
   const int NRT = dg::kCanvas * G / R;
-  // The natural plan never exceeds T + B*Hkv*NRT units whatever the prefixes.
   int64_t units = (int64_t)target_units(shape->dtype) + (int64_t)shape->batch * shape->n_heads_kv * NRT;
   const int forced = forced_split_keys();
   if (forced) {
     const int64_t S = (max_prefix_len + dg::kCanvas + forced - 1) / forced;
     units = std::max<int64_t>(units, S * shape->batch * shape->n_heads_kv * NRT);
   }
-  return (size_t)units * R * (shape->head_dim + 2) * sizeof(float);
+  return (size_t)units * R * partial_row_bytes(shape);
 }
 
 dg_status dg_canvas_attn(const dg_shape* shape, const void* q, const dg_kv* kv_cache,

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, Plan plan) {
       *(float4*)(op + 4 * c) =
           make_float4(o[4 * c] * inv, o[4 * c + 1] * inv, o[4 * c + 2] * inv, o[4 * c + 3] * inv);
   } else {
-    float* po = a.part_o + ((int64_t)U * R + lane) * D;
+    float* po = (float*)a.part_o + ((int64_t)U * R + lane) * D;
 #pragma unroll
     for (int c = 0; c < D4; c++)
       *(float4*)(po + 4 * c) =

@@ -27,8 +27,15 @@ struct SeqPlan {
   int32_t unit_base;   // first logical unit index of this sequence
 };
 
+// bf16 kernel shapes (eight waves, 32 packed rows per wave): packed rows per
+// unit = 32 x row groups; the remaining waves split the unit's keys.
+enum { kVariantR256 = 0, kVariantR128 = 1, kVariantR64 = 2, kNumVariants = 3 };
+constexpr int kDefaultVariant = kVariantR128;
+inline int variant_rows(int v) { return v == kVariantR256 ? 256 : (v == kVariantR64 ? 64 : 128); }
+
 struct Plan {
   int32_t batch;
+  int32_t variant;      // bf16 kernel shape (kVariant*); rows_per_unit follows from it
   int32_t n_units;      // total logical units = grid size of the attention kernel
   int32_t n_rowtiles;   // NRT = 256*G / R
   int32_t rows_per_unit;// R
@@ -44,7 +51,9 @@ struct AttnArgs {
   void* k_append;       // commit only: cache K/V written at rows L..L+255 (else null)
   void* v_append;
   void* out;            // [B][256][Hq][D]
-  float* part_o;        // [n_units][R][D] normalised partial outputs
+  void* part_o;         // [n_units][R][D] normalised partial outputs: bf16 for the
+                        // bf16 path (the output is rounded to bf16 anyway), fp32 for
+                        // the fp32 path
   float* part_ml;       // [n_units][R][2]: max (log2 domain) and sum
   int64_t cap;
   int32_t n_heads_q;
@@ -58,8 +67,7 @@ int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal
 int launch_attn_f32(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream);
 int launch_merge(const AttnArgs& a, const Plan& p, int head_dim, bool bf16_out, void* stream);
 
-// Rows per unit and key granule of each kernel family.
-constexpr int kRowsBf16 = 256;
+// Rows per unit of the fp32 kernel and the key granule of every kernel.
 constexpr int kRowsF32 = 64;
 constexpr int kKeyGranule = 32;
 

@@ -8,9 +8,9 @@
 // the canvas (or block) tile of one row merge into attention over [cache ;
 // canvas] ("DiffusionGemma Technical Report", paperfeed.app summary, section
 // "The mechanism: an AR model turned inside out").  Splits without keys carry
-// l_s = 0 and drop out.  Memory-bound: every thread handles four adjacent
-// head_dim elements of one row, so partial reads and output writes are
-// contiguous per row.
+// l_s = 0 and drop out.  Memory-bound: every thread handles one 16-byte chunk
+// of a row (eight bf16 or four fp32 head_dim elements), so partial reads and
+// output writes are contiguous per row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,14 +19,17 @@
 namespace dg {
 namespace {
 
-template <int D, bool BF16OUT>
+// Partial rows are bf16 for the bf16 path and fp32 for the fp32 path; each thread
+// combines 8 (bf16) or 4 (fp32) adjacent head_dim elements of one row.
+template <int D, bool BF16>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
-  constexpr int TPR = D / 4;        // threads per row
-  constexpr int RPB = 256 / TPR;    // rows per block
+  constexpr int EPT = BF16 ? 8 : 4;  // elements per thread
+  constexpr int TPR = D / EPT;       // threads per row
+  constexpr int RPB = 256 / TPR;     // rows per block
   const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = Hq / Hkv;
   const int rows_per_seq = Hkv * kCanvas * G;
   const int64_t grow = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int d4 = threadIdx.x % TPR;
+  const int dq = threadIdx.x % TPR;
   if (grow >= (int64_t)plan.batch * rows_per_seq) return;
   const int b = (int)(grow / rows_per_seq);
   const int rem = (int)(grow % rows_per_seq);
@@ -37,43 +40,67 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
   const int rt = p / R, pr = p % R;
   const int u0 = sp.unit_base + g * sp.n_splits * NRT + rt;
 
-  float M = -INFINITY;
-  for (int s = 0; s < sp.n_splits; s++)
-    M = fmaxf(M, a.part_ml[((int64_t)(u0 + s * NRT) * R + pr) * 2]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float wsum = 0.f;
-  for (int s = 0; s < sp.n_splits; s++) {
-    const int64_t base = (int64_t)(u0 + s * NRT) * R + pr;
-    const float2 ml = *(const float2*)(a.part_ml + base * 2);
-    const float w = exp2f(ml.x - M) * ml.y;
-    if (w == 0.f) continue;
-    const float4 v = *(const float4*)(a.part_o + base * D + 4 * d4);
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
-    wsum += w;
+  // Splits are visited in batches of 8 with all loads of a batch in flight at
+  // once; a running max keeps the weights bounded (partials carry finite maxima).
+  constexpr int BATCH = 8;
+  float M = -1e30f, wsum = 0.f;
+  float acc[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; e++) acc[e] = 0.f;
+  for (int s0 = 0; s0 < sp.n_splits; s0 += BATCH) {
+    float2 ml[BATCH];
+    uint4 v[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; j++) {
+      if (s0 + j < sp.n_splits) {
+        const int64_t base = (int64_t)(u0 + (s0 + j) * NRT) * R + pr;
+        ml[j] = *(const float2*)(a.part_ml + base * 2);
+        v[j] = BF16 ? *(const uint4*)((const uint16_t*)a.part_o + base * D + EPT * dq)
+                    : *(const uint4*)((const float*)a.part_o + base * D + EPT * dq);
+      } else {
+        ml[j] = make_float2(-1e30f, 0.f);
+        v[j] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < BATCH; j++) Mb = fmaxf(Mb, ml[j].x);
+    const float r = exp2f(M - Mb);
+#pragma unroll
+    for (int e = 0; e < EPT; e++) acc[e] *= r;
+    wsum *= r;
+#pragma unroll
+    for (int j = 0; j < BATCH; j++) {
+      const float w = exp2f(ml[j].x - Mb) * ml[j].y;
+      const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int e = 0; e < EPT; e++) {
+        const float x = BF16 ? __uint_as_float((e & 1) ? (wd[e / 2] & 0xffff0000u) : (wd[e / 2] << 16))
+                             : __uint_as_float(wd[e]);
+        acc[e] = fmaf(w, x, acc[e]);
+      }
+      wsum += w;
+    }
+    M = Mb;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int i = p / G, hh = p % G;
-  const int64_t off = ((int64_t)(b * kCanvas + i) * Hq + g * G + hh) * D + 4 * d4;
-  if (BF16OUT) {
-    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-    bf16x4 v;
-    v[0] = (__bf16)(acc.x * inv);
-    v[1] = (__bf16)(acc.y * inv);
-    v[2] = (__bf16)(acc.z * inv);
-    v[3] = (__bf16)(acc.w * inv);
-    *(bf16x4*)((uint16_t*)a.out + off) = v;
+  const int64_t off = ((int64_t)(b * kCanvas + i) * Hq + g * G + hh) * D + EPT * dq;
+  if (BF16) {
+    typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; e++) o[e] = (__bf16)(acc[e % EPT] * inv);
+    *(bf16x8*)((uint16_t*)a.out + off) = o;
   } else {
     *(float4*)((float*)a.out + off) =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        make_float4(acc[0] * inv, acc[1 % EPT] * inv, acc[2 % EPT] * inv, acc[3 % EPT] * inv);
   }
 }
 
 template <int D, bool BF16OUT>
 int launch_t(const AttnArgs& a, const Plan& p, hipStream_t st) {
-  constexpr int RPB = 256 / (D / 4);
+  constexpr int RPB = 256 / (D / (BF16OUT ? 8 : 4));
   const int64_t rows = (int64_t)p.batch * a.n_heads_q * kCanvas;
   const int blocks = (int)((rows + RPB - 1) / RPB);
   hipLaunchKernelGGL((merge_kernel<D, BF16OUT>), dim3(blocks), dim3(256), 0, st, a, p);

@@ -18,7 +18,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdg.so")
+# DG_LIBRARY selects another build of the same library (for example a variant
+# compiled with different tuning flags); the default is the in-tree build.
+LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(_HERE, "libdg.so")
 
 DG_BF16, DG_F32 = 0, 1
 N_CANVAS = 256
