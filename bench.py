@@ -17,6 +17,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,130 @@ sys.path.insert(0, ROOT)
 METRIC = "canvas-step attn TFLOP/s + canvas positions/s at L=8k, bs=1; % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+# HBM traffic of the dominant kernel comes from rocprofv3 counter runs
+# (FETCH_SIZE and WRITE_SIZE per dispatch, calibrated against a plain copy of
+# known size) recorded in this file together with a hash of the kernel source;
+# it is reported only while the source still matches.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "canvas_attn_l8k_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
+                  for f in ("dg_attn_bf16.hip", "dg_internal.h")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Bytes per launch of the canvas attention kernel from the counter file, or
+    None when the file is absent or was taken on another version of the kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if kv["kernel_source_hash"] != kernel_source_hash():
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of known size (the counter calibration run)."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
+def _counter_per_dispatch(folder, counter, name_part):
+    """Mean value of one counter over the dispatches of kernels whose name holds
+    name_part, from a rocprofv3 --pmc csv folder."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                    vals[(f, r["Dispatch_Id"])] = vals.get((f, r["Dispatch_Id"]), 0.0) + \
+                        float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for '{name_part}' under {folder}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+ATTN_KERNEL = "attn_bf16_kernel<128, false"
+
+
+def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib):
+    copy_bytes = int(copy_mib) * (1 << 20)
+    f_kib, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", ATTN_KERNEL)
+    w_kib, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", ATTN_KERNEL)
+    cf_kib, _ = _counter_per_dispatch(cfetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw_kib, _ = _counter_per_dispatch(cwrite_dir, "WRITE_SIZE", "copyBuffer")
+    f_scale = copy_bytes / (cf_kib * 1024.0)
+    w_scale = copy_bytes / (cw_kib * 1024.0)
+    fetch = f_kib * 1024.0 * f_scale
+    write = w_kib * 1024.0 * w_scale
+    lines = [
+        "# HBM traffic of the canvas attention kernel (canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)",
+        "# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of",
+        "#   python3 bench.py --steps 2 --warmup 1 --profile-steps",
+        "# calibrated with the same counters on a plain device-to-device copy of known size",
+        f"#   python3 bench.py --copy-probe {copy_mib}",
+        "# (each scale = copy bytes / counter bytes of that copy); written by",
+        "#   python3 bench.py --summarize-counters FETCH WRITE COPY_FETCH COPY_WRITE MIB",
+        f"kernel: {ATTN_KERNEL}...>",
+        f"kernel_source_hash: {kernel_source_hash()}",
+        f"dispatches_fetch: {nf}",
+        f"dispatches_write: {nw}",
+        f"fetch_kib_per_dispatch: {f_kib:.1f}",
+        f"write_kib_per_dispatch: {w_kib:.1f}",
+        f"copy_bytes: {copy_bytes}",
+        f"copy_fetch_kib: {cf_kib:.1f}",
+        f"copy_write_kib: {cw_kib:.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"fetch_bytes_per_launch: {fetch:.0f}",
+        f"write_bytes_per_launch: {write:.0f}",
+        f"traffic_bytes_per_launch: {fetch + write:.0f}",
+    ]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_trace(stats_csv, out_txt):
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    keep = [r for r in rows if "dg::" in r["Name"] or "copyBuffer" in r["Name"]]
+    lines = ["# rocprofv3 --kernel-trace --stats summary (kernels of this library)",
+             "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+             "-d <dir> -o run -- python3 <repo>/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+             f"{'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_pct':>9}  kernel"]
+    for r in keep:
+        lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.3f} "
+                     f"{float(r['MinNs']) / 1e3:10.3f} {float(r['MaxNs']) / 1e3:10.3f} "
+                     f"{float(r['Percentage']):9.2f}  {r['Name'][:110]}")
+    with open(out_txt, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def step_flops(B, Hq, L, D, Nc=256):
@@ -55,13 +180,30 @@ def main():
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only run the timed cycles (for rocprofv3 runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device to device 5 times (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH",
+                                                              "COPY_WRITE", "COPY_MIB"),
+                    help="write the traffic file from four rocprofv3 --pmc output folders")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "OUT_TXT"),
+                    help="write a kernel summary from a rocprofv3 --stats kernel_stats.csv")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the canvas "
               "attention path has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import canvas_attention_amd.dg as dg
     from canvas_attention_amd import synth
@@ -163,7 +305,8 @@ def main():
                        if n_cmerge else 0.0},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(),
                      "kernel": "attn_bf16_kernel<128,false> (canvas step, L=8192)",
                      "algorithmic_flop_per_launch": fl_step,
                      "hbm_frac": round(step_bytes(B, Hq, Hkv, Lv, D) / (attn_us * 1e-6) / 1e9
@@ -176,8 +319,9 @@ def main():
 
 
 def cpu_baseline(name, budget_s):
-    """The CPU fp64 oracle on a bounded sample of the same canvas step: whole
-    canvas rows (all heads) in chunks until the time budget is spent."""
+    """The CPU fp64 oracle on a bounded sample of the same workload: whole canvas
+    steps of the block cycle (each with its own seeded canvas Q/K/V, all 256
+    positions and all heads), one after another until the time budget is spent."""
     import oracle
     from canvas_attention_amd import synth
     w = synth.WORKLOADS[name]
@@ -185,25 +329,21 @@ def cpu_baseline(name, budget_s):
     L = synth.prefix_lengths(name)
     Lv = int(L[0])
     kc, vc = synth.cache(seed, L, Lv + 256, Hkv, D, "bf16")
-    q, kn, vn = synth.canvas(seed, B, Hq, Hkv, D, "bf16")
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    done_rows = 0
+    steps = [synth.canvas(seed, B, Hq, Hkv, D, "bf16", step=s) for s in range(w["steps"])]
+    done = 0
     t_start = time.perf_counter()
     elapsed = 0.0
-    i0 = 0
-    while elapsed < budget_s and i0 < 256:
-        rows = np.array([(0, i, h) for i in range(i0, min(256, i0 + 16)) for h in range(Hq)],
-                        np.int32)
-        oracle.canvas_attn(q, kc, vc, L, kn, vn, rows=rows)
-        done_rows += len(rows)
-        i0 += 16
+    while elapsed < budget_s:
+        q, kn, vn = steps[done % len(steps)]
+        oracle.canvas_attn(q, kc, vc, L, kn, vn)
+        done += 1
         elapsed = time.perf_counter() - t_start
-    flops = done_rows * 4.0 * (Lv + 256) * D
-    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done_rows} of {B * 256 * Hq} query rows of one canvas step at L={Lv} "
-                      f"({done_rows // Hq} canvas positions, all {Hq} heads), {elapsed:.1f} s; "
-                      f"canvas positions/s {done_rows / Hq / elapsed:.2f}"}
+    flops = done * step_flops(B, Hq, Lv, D)
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} whole canvas steps of the L={Lv} block cycle (B={B}, 256 "
+                      f"positions, Hq={Hq}, Hkv={Hkv}, D={D}) in {elapsed:.1f} s: "
+                      f"{done * B * 256 / elapsed:.1f} canvas positions/s"}
 
 
 if __name__ == "__main__":

@@ -11,10 +11,9 @@
 //     L..L+255 by the same launch (the finished canvas is appended).
 //
 // Design (CDNA4):
-//   * A workgroup is NW wave64s = WM row groups x WK key groups.  Each wave owns
-//     32*NB packed query rows held in VGPRs.  With NW = 8 two waves share each
-//     SIMD, so one wave's MFMAs overlap the other's softmax arithmetic and the
-//     register budget (256 per wave) keeps every MFMA in VGPR form.
+//   * A workgroup is eight wave64s = WM row groups x WK key groups; each wave
+//     owns 32 packed query rows (its Q operands stay in VGPRs) and walks its key
+//     group's 32-key chunks.
 //   * GQA packing: the G query heads of kv head g are rows p = i*G + hh of one
 //     256*G-row matrix, so every K/V tile read from LDS feeds all query heads of
 //     the group at once.
@@ -25,15 +24,23 @@
 //     packed to bf16, are used directly as the B operand of O^T += V^T P^T
 //     (K = 16 keys per MFMA): the key order inside each MFMA is permuted
 //     consistently for P and V, which costs nothing because keys are summed over.
-//   * K/V tiles stream HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging)
-//     into an NST-slot ring, one workgroup barrier per tile.  Whole tiles inside
-//     the cache or the canvas use a scalar base plus precomputed 32-bit lane
-//     offsets; only a tile that crosses the cache/canvas seam or the end of the
-//     unit takes the per-lane path.  Rows are stored densely (D*2 bytes) with an
-//     XOR swizzle of the 16-byte chunks so that the K operand reads
-//     (ds_read_b128, one key row per lane) and the V operand reads
-//     (ds_read_b64_tr_b16, the gfx950 transposing LDS read) are bank-conflict
-//     free.
+//   * Ping-pong: waves w and w+4 share a SIMD.  Each chunk is split into an MFMA
+//     phase X (value product of chunk k, scores of chunk k+1: sixteen MFMAs) and
+//     a vector phase Y (softmax of chunk k+1, LDS operand reads for the next X).
+//     Two workgroup barriers per chunk keep the two halves of the workgroup half
+//     a chunk apart, so on every SIMD one wave runs X while the other runs Y: the
+//     matrix pipe and the vector ALU work at the same time.  The MFMA phase runs
+//     at raised wave priority.
+//   * K/V stream HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a
+//     ring of NSLOT stages (one 32-key tile per key group each); a stage is
+//     refilled as soon as the barrier after its last operand read has passed,
+//     which keeps NSLOT-2 chunks of loads in flight.  Whole tiles inside the
+//     cache or the canvas use a scalar base plus precomputed 32-bit lane offsets;
+//     only a tile that crosses the cache/canvas seam or the end of the unit takes
+//     the per-lane path.  Rows are stored densely (D*2 bytes) with an XOR swizzle
+//     of the 16-byte chunks so that the K operand reads (ds_read_b128, one key row
+//     per lane) and the V operand reads (ds_read_b64_tr_b16, the gfx950
+//     transposing LDS read) are bank-conflict free.
 //   * Softmax runs in the log2 domain with a lazily raised reference max: a
 //     chunk's exact max is always formed, but the output is rescaled only when it
 //     exceeds the reference by more than 64 (so every exponential stays <= 2^64);
@@ -41,8 +48,9 @@
 //     The result is exact attention; only the point at which the max is folded
 //     in moves.
 //   * Key groups of a workgroup are merged through LDS at the end; the unit
-//     writes its normalised partial rows (fp32) plus (max, sum), or the final
-//     bf16 output when the sequence has a single split.
+//     writes its normalised rows (bf16) plus (max, sum) as a partial, or the final
+//     output when the sequence has a single split, through an LDS staging area so
+//     that every store is a whole 128-byte row segment.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -108,18 +116,6 @@ struct State {
   float lsum;    // sum of this lane's exponentials (the partner lane holds the rest)
 };
 
-// Where a key group's tiles come from.
-struct TileSrc {
-  const char *kc, *vc;  // cache K/V of (sequence, kv head), row 0
-  const char *kn, *vn;  // canvas/block K/V of (sequence, kv head), row 0
-  int rsb;              // bytes between consecutive rows (Hkv * D * 2)
-  int L;                // cache rows; key j >= L is canvas row j - L
-  int kstop;            // end of the unit's keys; later rows are clamped onto kstop-1
-  uint32_t lrs;         // lane row offset (lane / CH) * rsb
-  int lp;               // lane physical chunk (lane % CH)
-  int lr;               // lane row within one load instruction (lane / CH)
-};
-
 // One global_load_lds_dwordx4: every lane copies 16 bytes from its global address
 // into LDS at m0 + 16*lane.  Issued from inline asm so that the compiler does not
 // see an LDS write it cannot disambiguate from the operand reads of the other
@@ -136,6 +132,12 @@ __device__ __forceinline__ void gll_vaddr(const char* vaddr, uint32_t lds) {
                : "memory");
 }
 
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint64_t v = (uint64_t)(uintptr_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -143,60 +145,107 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Issues this wave's share of the global_load_lds instructions that copy one tile
-// (TK keys of K, then TK keys of V) into LDS at kt.  Each instruction moves 1 KB:
-// lane l writes 16 bytes at kt + 1024*instr + 16*l, i.e. tile row l / CH, physical
-// chunk l % CH, and fetches the logical chunk that the swizzle stores there
-// (K: chunk ^ (row % CH); V: chunk ^ 4*(row % 4)).
-template <int D, int TK, int WM>
-__device__ __forceinline__ void issue_tile(uint32_t kt, int tkey0, const TileSrc& t, int rg) {
-  constexpr int CH = D / 8, RPI = 1024 / (D * 2), IPT = TK / RPI;  // instructions per K tile
-  constexpr int GLL = 2 * IPT / WM;
-  const bool in_cache = tkey0 + TK <= t.L && tkey0 + TK <= t.kstop;
-  const bool in_canvas = tkey0 >= t.L && tkey0 + TK <= t.kstop;
-  if (in_cache || in_canvas) {
-    // whole tile from one tensor: scalar base + 32-bit lane offset
-    const char* kb = in_cache ? t.kc + (int64_t)tkey0 * t.rsb : t.kn + (int64_t)(tkey0 - t.L) * t.rsb;
-    const char* vb = in_cache ? t.vc + (int64_t)tkey0 * t.rsb : t.vn + (int64_t)(tkey0 - t.L) * t.rsb;
+// This wave's share of the global_load_lds instructions that fill one ring stage:
+// for every key group kt a 32-key tile, K rows then V rows.  Each instruction
+// moves 1 KB: lane l writes 16 bytes at dst + 16*l, i.e. tile row l / CH of the
+// instruction's row block, physical chunk l % CH, and fetches the logical chunk
+// that the swizzle stores there (K: chunk ^ (row % CH); V: chunk ^ 4*(row % 4)).
+// Everything that does not depend on the stage is computed once per wave; per
+// stage only the byte offset of its first key is formed, and a stage lying
+// wholly in the cache or wholly in the canvas (every stage but the one at the
+// seam and the unit's last) is issued as scalar base + 32-bit lane offset.
+// The ring holds the K tiles of every stage in its first 64 KB and the V tiles in
+// the second: stage s, key group kt at s*WK*TILEB + kt*TILEB (+ kVRegion for V),
+// so that every operand read is a per-lane base plus an immediate offset.
+constexpr uint32_t kVRegion = 65536;
+
+template <int D, int WK>
+struct StageLoads {
+  static constexpr int CH = D / 8, ROWB = D * 2, RPI = 1024 / ROWB, IPT = 32 / RPI;
+  static constexpr int TILEB = 32 * ROWB, GPW = WK * 2 * IPT / 8;
+  uint64_t cb[GPW];         // cache K or V base of (sequence, kv head) for instruction e
+  uint64_t nb[GPW];         // canvas/block K or V base minus L rows for instruction e
+  uint32_t rowoff[GPW];     // (kt*32 + first row) * row stride of instruction e
+  uint32_t dst[GPW];        // LDS offset of instruction e within a stage
+  uint32_t lane[GPW];       // lane byte offset: row (lane / CH) * stride + swizzled chunk
+  int32_t krow[GPW];        // lane's key offset within the stage (kt*32 + row)
+  uint32_t lrs;             // (lane / CH) * row stride
+  int32_t rsb, L, kstop;
+};
+
+template <int D, int WK>
+__device__ __forceinline__ void stage_loads_init(StageLoads<D, WK>& sl, const char* kc,
+                                                 const char* vc, const char* kn, const char* vn,
+                                                 int rsb, int L, int kstop, int wave, int lane) {
+  using SL = StageLoads<D, WK>;
+  const int lr = lane / SL::CH, lp = lane % SL::CH;
+  sl.rsb = rsb;
+  sl.L = L;
+  sl.kstop = kstop;
+  sl.lrs = (uint32_t)lr * (uint32_t)rsb;
+  const uint64_t ukc = (uint64_t)(uintptr_t)kc, uvc = (uint64_t)(uintptr_t)vc;
+  const uint64_t ukn = (uint64_t)(uintptr_t)kn - (uint64_t)L * (uint64_t)rsb;
+  const uint64_t uvn = (uint64_t)(uintptr_t)vn - (uint64_t)L * (uint64_t)rsb;
 #pragma unroll
-    for (int e = 0; e < GLL; e++) {
-      const int instr = rg + WM * e;
-      const bool isv = instr >= IPT;
-      const int ri = instr % IPT;
-      const int r0 = ri * RPI;  // first tile row of this instruction (uniform)
-      const int sw = isv ? ((4 * (t.lr & 3)) & (CH - 1)) : ((r0 + t.lr) & (CH - 1));
-      const uint32_t off = t.lrs + 16u * (uint32_t)(t.lp ^ sw);
-      const char* base = uniform_ptr((isv ? vb : kb) + (int64_t)r0 * t.rsb);
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(kt + (isv ? TK * D * 2 : 0) + ri * 1024);
-      gll_saddr(base, off, dst);
+  for (int e = 0; e < SL::GPW; e++) {
+    const int instr = wave + 8 * e;  // wave-uniform
+    const int kt = instr / (2 * SL::IPT), w2 = instr % (2 * SL::IPT);
+    const bool isv = w2 >= SL::IPT;
+    const int ri = w2 % SL::IPT;
+    const int r0 = ri * SL::RPI;
+    sl.cb[e] = uniform64(isv ? uvc : ukc);
+    sl.nb[e] = uniform64(isv ? uvn : ukn);
+    sl.rowoff[e] = (uint32_t)((kt * 32 + r0) * rsb);
+    sl.dst[e] = (uint32_t)((isv ? kVRegion : 0) + kt * SL::TILEB + ri * 1024);
+    const int r = r0 + lr;
+    const int sw = isv ? ((4 * (r & 3)) & (SL::CH - 1)) : (r & (SL::CH - 1));
+    sl.lane[e] = (uint32_t)lr * (uint32_t)rsb + 16u * (uint32_t)(lp ^ sw);
+    sl.krow[e] = kt * 32 + r;
+  }
+}
+
+// Issues the wave's loads of one stage (keys from skey0, WK tiles) into the LDS
+// slot.  Tiles past the unit's last key are loaded too (rows clamped onto the
+// unit's last key) so that each wave always has the same number of loads per
+// stage in flight.
+template <int D, int WK>
+__device__ __forceinline__ void issue_stage(uint32_t slot, int skey0, const StageLoads<D, WK>& sl) {
+  using SL = StageLoads<D, WK>;
+  const int send = skey0 + 32 * WK;
+  const bool in_cache = send <= sl.L && send <= sl.kstop;
+  const bool in_canvas = skey0 >= sl.L && send <= sl.kstop;
+  if (in_cache || in_canvas) {
+    const uint64_t koff = (uint64_t)(int64_t)skey0 * (uint64_t)sl.rsb;
+#pragma unroll
+    for (int e = 0; e < SL::GPW; e++) {
+      const uint64_t tb = (in_cache ? sl.cb[e] : sl.nb[e]) + koff + sl.rowoff[e];
+      gll_saddr(uniform_ptr((const char*)(uintptr_t)tb), sl.lane[e],
+                __builtin_amdgcn_readfirstlane(slot + sl.dst[e]));
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < GLL; e++) {
-      const int instr = rg + WM * e;
-      const bool isv = instr >= IPT;
-      const int ri = instr % IPT;
-      const int r = ri * RPI + t.lr;
-      const int c = isv ? (t.lp ^ ((4 * (r & 3)) & (CH - 1))) : (t.lp ^ (r & (CH - 1)));
-      const int key = min(tkey0 + r, t.kstop - 1);
-      const char* row = key < t.L ? (isv ? t.vc : t.kc) + (int64_t)key * t.rsb
-                                  : (isv ? t.vn : t.kn) + (int64_t)(key - t.L) * t.rsb;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(kt + (isv ? TK * D * 2 : 0) + ri * 1024);
-      gll_vaddr(row + 16 * c, dst);
+    for (int e = 0; e < SL::GPW; e++) {
+      const int key = min(skey0 + sl.krow[e], sl.kstop - 1);
+      const uint64_t base = key < sl.L ? sl.cb[e] : sl.nb[e];
+      const uint64_t row = base + (uint64_t)(int64_t)key * (uint64_t)sl.rsb;
+      // the row is the lane's own here: keep only the swizzled chunk of the lane offset
+      gll_vaddr((const char*)(uintptr_t)(row + (sl.lane[e] - sl.lrs)),
+                __builtin_amdgcn_readfirstlane(slot + sl.dst[e]));
     }
   }
 }
 
 // V^T operands of one 32-key chunk: vop[mb][t] holds, in lane (d, h), the values
 // of keys 16t + 8r + 4h + e (k-slot 4r + e) at head_dim 32mb + d, read with the
-// transposing ds_read_b64_tr_b16.
+// transposing ds_read_b64_tr_b16.  vbase[mb] is the lane's address in stage 0;
+// off (a compile-time constant in the unrolled loop) selects the stage.
 template <int D>
-__device__ __forceinline__ void load_v_operands(uint32_t vbase, const uint32_t (&voff)[D / 32],
+__device__ __forceinline__ void load_v_operands(const uint32_t (&vbase)[D / 32], uint32_t off,
                                                 bf16x8 (&vop)[D / 32][2]) {
   constexpr int ROWB = D * 2, MB = D / 32;
 #pragma unroll
   for (int mb = 0; mb < MB; mb++) {
-    const LDS_AS char* p = (const LDS_AS char*)(uintptr_t)(vbase + voff[mb]);
+    const LDS_AS char* p = (const LDS_AS char*)(uintptr_t)(vbase[mb] + off);
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p + 16 * t * ROWB));
@@ -234,13 +283,14 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
 }
 
 // K operands of one 32-key chunk: kop[ks] = key row n, logical chunk
-// (D/16)*h + ks (the A operand of S^T = K Q^T).
+// (D/16)*h + ks (the A operand of S^T = K Q^T); kbase[ks] is the lane's address
+// in stage 0 and off selects the stage.
 template <int D>
-__device__ __forceinline__ void load_k_operands(uint32_t kbase, const uint32_t (&koff)[D / 16],
+__device__ __forceinline__ void load_k_operands(const uint32_t (&kbase)[D / 16], uint32_t off,
                                                 bf16x8 (&kop)[D / 16]) {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ks++)
-    kop[ks] = *(const LDS_AS bf16x8*)(uintptr_t)(kbase + koff[ks]);
+    kop[ks] = *(const LDS_AS bf16x8*)(uintptr_t)(kbase[ks] + off);
 }
 
 template <int D>
@@ -253,16 +303,14 @@ __device__ __forceinline__ void scores(const bf16x8 (&kop)[D / 16], const bf16x8
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qr[ks], s, 0, 0, 0);
 }
 
-// Masks a chunk's scores (ragged end of the unit; block keys past the diagonal
-// for the commit), folds the chunk max into the reference max when it rises by
-// more than the threshold, and returns nothing else: the exponentials follow.
+// Masks a chunk's scores when asked (ragged end of the unit; block keys past
+// the diagonal for the commit), folds the chunk max into the reference max when
+// it rises by more than the threshold, and returns nothing else: the
+// exponentials follow.
 template <int MB, bool CAUSAL>
-__device__ __forceinline__ void prepare_scores(f32x16& s, int key0, int kstop, int L,
-                                               int wave_qi_min, int qi, int h, float c2,
-                                               State<MB>& acc) {
-  const bool tail = key0 + 32 > kstop;
-  const bool diag = CAUSAL && (key0 + 31 - L > wave_qi_min);
-  if (tail || diag) {
+__device__ __forceinline__ void prepare_scores(f32x16& s, bool masked, int key0, int kstop, int L,
+                                               int qi, int h, float c2, State<MB>& acc) {
+  if (masked) {
 #pragma unroll
     for (int i = 0; i < 16; i++) {
       const int key = key0 + 8 * (i / 4) + 4 * h + (i % 4);
@@ -288,20 +336,22 @@ __device__ __forceinline__ void prepare_scores(f32x16& s, int key0, int kstop, i
 }
 
 // exp2(s*c - m) packed to bf16 (the B operand of the value product); the row
-// sum accumulates the packed values with dot2.
+// sum accumulates the packed values with dot2.  Computed in place, stage by
+// stage, so that the sixteen exponentials are independent and pipeline.
 template <int MB>
-__device__ __forceinline__ void numerators(const f32x16& s, float c2, State<MB>& acc,
-                                           bf16x8 (&pb)[2]) {
+__device__ __forceinline__ void numerators(f32x16& s, float c2, State<MB>& acc, bf16x8 (&pb)[2]) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const float nm = -acc.mlog;
+#pragma unroll
+  for (int i = 0; i < 16; i++) s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, nm));
   float sum = acc.lsum;
 #pragma unroll
   for (int t = 0; t < 2; t++) {
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
       bf16x2 pr;
-      pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * t + j], c2, nm));
-      pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * t + j + 1], c2, nm));
+      pr[0] = (__bf16)s[8 * t + j];
+      pr[1] = (__bf16)s[8 * t + j + 1];
       pb[t][j] = pr[0];
       pb[t][j + 1] = pr[1];
       sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
@@ -320,37 +370,42 @@ __device__ __forceinline__ void values(const bf16x8 (&vop)[MB][2], const bf16x8 
       acc.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[mb][t], pb[t], acc.o[mb], 0, 0, 0);
 }
 
-// The kernel.  Waves process a stream of 32-key chunks; chunk i of a wave lies in
-// stage st = i / CPT (tile st*WK + kg of the unit) at position i % CPT.  The
-// stream is software-pipelined: while the exponentials of chunk i are formed,
-// the score MFMAs of chunk i+1 are issued in the same basic block, interleaved by
-// the scheduler (one MFMA per group of VALU instructions), then chunk i's value
-// MFMAs follow.  K/V tiles sit in a 2-slot ring: entering a stage waits for its
-// tile, then refills the slot of the previous stage, whose last LDS reads (the V
-// operands of its final chunk) completed before the barrier.
-template <int D, bool CAUSAL, int WM, int WK, int TK>
+// The kernel.  Wave (rg, kg) processes chunk k = tile k*WK + kg of the unit for
+// k = 0 .. nstages-1; chunk k lives in ring stage k.  Per chunk a wave runs
+//   X(k): O += V(k) P(k) (8 MFMAs), S(k+1) = K(k+1) Q^T (8 MFMAs)
+//   Y(k): V(k+1) and K(k+2) operand reads, softmax of S(k+1) -> P(k+1)
+// Workgroup barriers split time into half-chunk phases; waves 0-3 (group 0) and
+// waves 4-7 (group 1) run the same sequence one phase apart, so that while one
+// wave of a SIMD is in X the other is in Y.
+// Ring protocol: every barrier first waits for the wave's LDS reads, so the
+// last reads of stage j (group 1's V(j), in the phase after barrier 2j) are done
+// at barrier 2j+1, after which stage j+NSLOT may overwrite it; the first reads
+// of stage j+2 (group 0's K(j+2), after barrier 2j+1) need it complete, so
+// before barrier 2j+1 every wave waits for its own loads of stage j+2, with at
+// most the NSLOT-3 later stages left in flight.
+template <int D, bool CAUSAL, int WM, int WK, int NSLOT>
 __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan) {
   static_assert(WM * WK == 8, "eight waves: row groups x key groups");
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static_assert(NSLOT >= 4, "the ring keeps at least two stages in flight");
   constexpr int NT = 512;               // threads per workgroup
   constexpr int R = 32 * WM;            // packed rows per unit
   constexpr int KS = D / 16;            // MFMA k-steps over head_dim
   constexpr int CH = D / 8;             // 16-byte chunks per K/V row
   constexpr int MB = D / 32;            // 32-row blocks of O^T
   constexpr int ROWB = D * 2;           // bytes per K/V row
-  constexpr int TILEB = TK * ROWB;      // bytes per K (or V) tile
-  constexpr int RPI = 1024 / ROWB;      // rows one global_load_lds covers (64 lanes x 16 B)
-  constexpr int GLL = 2 * TK / RPI / WM;// global_load_lds per wave per tile
-  constexpr int CPT = TK / 32;          // chunks per tile
-  static_assert(GLL >= 1 && (2 * TK / RPI) % WM == 0, "tile load split");
-  constexpr int SLOTB = WK * 2 * TILEB; // one ring slot: K and V tiles of every key group
+  constexpr int TILEB = 32 * ROWB;      // bytes per 32-key K (or V) tile
+  constexpr int SLOTB = WK * 2 * TILEB; // one ring stage: K and V tiles of every key group
+  constexpr int GPW = SLOTB / 1024 / 8; // global_load_lds per wave per stage
+  static_assert(GPW >= 1 && SLOTB % 8192 == 0, "stage load split");
   constexpr int PER = MB * 16 + 2;      // floats per lane in the key-group merge
   constexpr int MERGEB = (WK - 1) * WM * 64 * PER * 4;
-  static_assert(MERGEB <= 2 * SLOTB, "key-group merge fits in the ring");
-  __shared__ __attribute__((aligned(1024))) char ring[2 * SLOTB];
+  static_assert(MERGEB <= NSLOT * SLOTB, "key-group merge fits in the ring");
+  __shared__ __attribute__((aligned(1024))) char ring[NSLOT * SLOTB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
+  const int grp = wave >> 2;  // waves w and w+4 share a SIMD
   const int n = lane & 31, h = lane >> 5;
   const int rg = wave % WM, kg = wave / WM;
   const int U = xcd_remap(blockIdx.x, gridDim.x);
@@ -363,7 +418,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
   if (CAUSAL) kend = min(kend, L + (row0 + R - 1) / G + 1);
   const int kbeg = u.s * sp.split_keys;
   const int kstop = min(kbeg + sp.split_keys, kend);
-  const int ntiles = kstop > kbeg ? (kstop - kbeg + TK - 1) / TK : 0;
+  const int ntiles = kstop > kbeg ? (kstop - kbeg + 31) / 32 : 0;
   const int nstages = (ntiles + WK - 1) / WK;
 
   const int64_t cap = a.cap;
@@ -403,17 +458,12 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
     for (int ks = 0; ks < KS; ks++) qr[ks] = *(const bf16x8*)(qp + 8 * ks);
   }
 
-  TileSrc src;
-  src.kc = (const char*)(kc + ((int64_t)u.b * cap * Hkv + u.g) * D);
-  src.vc = (const char*)(vc + ((int64_t)u.b * cap * Hkv + u.g) * D);
-  src.kn = (const char*)(kn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D);
-  src.vn = (const char*)(vn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D);
-  src.rsb = Hkv * D * 2;
-  src.L = L;
-  src.kstop = kstop;
-  src.lr = lane / CH;
-  src.lp = lane % CH;
-  src.lrs = (uint32_t)(lane / CH) * (uint32_t)src.rsb;
+  StageLoads<D, WK> sl;
+  stage_loads_init<D, WK>(sl, (const char*)(kc + ((int64_t)u.b * cap * Hkv + u.g) * D),
+                          (const char*)(vc + ((int64_t)u.b * cap * Hkv + u.g) * D),
+                          (const char*)(kn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
+                          (const char*)(vn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
+                          Hkv * D * 2, L, kstop, wave, lane);
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
   const int wave_qi_min = (row0 + 32 * rg) / G;
   const int wave_qi_max = (row0 + 32 * rg + 31) / G;
@@ -429,83 +479,116 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
   acc.mlog = -1e30f;  // log2-domain reference max; finite so rescales never form inf-inf
   acc.lsum = 0.f;
 
-  char* slot0 = ring + kg * 2 * TILEB;
-  char* slot1 = ring + SLOTB + kg * 2 * TILEB;
-  const uint32_t lslot0 = lds_addr(slot0), lslot1 = lds_addr(slot1);
-  // chunk i of this wave: tile (i/CPT)*WK + kg, first key below
-  auto chunk_key = [&](int i) { return kbeg + ((i / CPT) * WK + kg) * TK + 32 * (i % CPT); };
-  auto chunk_ok = [&](int i) {
-    return (i / CPT) * WK + kg < ntiles && chunk_key(i) < klimit;
-  };
-  auto chunk_lds = [&](int i) {
-    return ((i / CPT) & 1 ? lslot1 : lslot0) + 32 * (i % CPT) * ROWB;
-  };
-
-  const int nchunks = nstages * CPT;
-  if (nstages > 0) {
-    if (kg < ntiles) issue_tile<D, TK, WM>(lslot0, kbeg + kg * TK, src, rg);
-    const bool second = 1 < nstages && WK + kg < ntiles;
-    if (second) issue_tile<D, TK, WM>(lslot1, kbeg + (WK + kg) * TK, src, rg);
-    if (second)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(GLL) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // Chunk k of this wave is tile t = k*WK + kg of the unit (keys kbeg + 32t ..).
+  // It holds visible keys iff k < nok; its scores need masking iff k >= kmask
+  // (ragged end of the unit, or for the commit a tile reaching past the
+  // diagonal of the wave's first query).
+  const int tvis = klimit > kbeg ? (klimit - kbeg + 31) / 32 : 0;
+  const int nok = tvis > kg ? (tvis - kg + WK - 1) / WK : 0;
+  int tmask = (kstop - kbeg) / 32;
+  if (CAUSAL) {
+    const int x = wave_qi_min + L - 31 - kbeg;
+    tmask = min(tmask, x >= 0 ? x / 32 + 1 : 0);
   }
-  // Consume the query registers before the loop: the compiler's own vmcnt wait for
-  // them lands here (it also covers the first prefetches, which were issued after
-  // the queries and were needed anyway); inside the loop such a wait would drain
-  // prefetches the compiler does not know about.
+  const int kmask = tmask > kg ? (tmask - kg + WK - 1) / WK : 0;
+
+  static_assert((NSLOT & (NSLOT - 1)) == 0, "ring of a power-of-two number of stages");
+  constexpr uint32_t SSTR = WK * TILEB;  // stage stride within the K (or V) region
+  static_assert(NSLOT * SSTR <= kVRegion, "K and V regions of the ring");
+  const uint32_t lring = lds_addr(ring);
+  auto stage_slot = [&](int slot) { return lring + (uint32_t)slot * SSTR; };
+  auto chunk_key = [&](int k) { return kbeg + (k * WK + kg) * 32; };
+  // per-lane operand addresses in stage 0 of this wave's key group
+  uint32_t kaddr[KS], vaddr[MB];
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) kaddr[ks] = lring + kg * TILEB + lo.k[ks];
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++) vaddr[mb] = lring + kVRegion + kg * TILEB + lo.v[mb];
+
+  // ---- prologue: every free stage of the ring is requested; stages 0 and 1
+  //      (the operands of the first chunk and the scores of the second) are waited for
+  const int npre = min(NSLOT, nstages);
+  for (int st = 0; st < npre; st++) issue_stage<D, WK>(stage_slot(st), kbeg + st * WK * 32, sl);
+  if (nstages >= NSLOT)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSLOT - 2) * GPW) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  // Consume the query registers here: the compiler's own vmcnt waits for them
+  // (which also cover every load issued after them) land before the loop, not in it.
 #pragma unroll
   for (int ks = 0; ks < KS; ks++) asm volatile("" ::"v"(qr[ks]));
-  f32x16 s_cur;
-  bf16x8 kop[KS];
-  if (nchunks > 0 && chunk_ok(0)) {
-    load_k_operands<D>(chunk_lds(0), lo.k, kop);
-    scores<D>(kop, qr, s_cur);
+
+  f32x16 s_nx;      // scores of the chunk the next softmax works on
+  bf16x8 kop[KS];   // K operands for the next score MFMAs
+  bf16x8 vop[MB][2];// V^T operands for the next value MFMAs
+  bf16x8 pb[2];     // packed exponentials for the next value MFMAs
+  if (0 < nok) {
+    load_k_operands<D>(kaddr, 0, kop);
+    scores<D>(kop, qr, s_nx);
+    load_v_operands<D>(vaddr, 0, vop);
   }
-  for (int i = 0; i < nchunks; i++) {
-    const bool ok = chunk_ok(i);
-    bf16x8 vop[MB][2];
-    if (ok) load_v_operands<D>(chunk_lds(i) + TILEB, lo.v, vop);
-    const int i1 = i + 1;
-    bool ok1 = false;
-    if (i1 < nchunks) {
-      if (i1 % CPT == 0) {
-        // entering stage st1: its tile must have landed in every wave's share;
-        // afterwards the previous stage's slot (all of its reads are done) is
-        // refilled with stage st1+1
-        const int st1 = i1 / CPT;
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        const int t2 = (st1 + 1) * WK + kg;
-        if (st1 + 1 < nstages && t2 < ntiles)
-          issue_tile<D, TK, WM>((st1 + 1) & 1 ? lslot1 : lslot0, kbeg + t2 * TK, src, rg);
-      }
-      ok1 = chunk_ok(i1);
-      if (ok1) load_k_operands<D>(chunk_lds(i1), lo.k, kop);
-    }
-    f32x16 s_next;
-    bf16x8 pb[2];
-    if (ok) {
-      prepare_scores<MB, CAUSAL>(s_cur, chunk_key(i), kstop, L, wave_qi_min, qi, h, c2, acc);
-      if (ok1) {
-        // one basic block: next chunk's score MFMAs interleaved with this chunk's
-        // exponentials
-        scores<D>(kop, qr, s_next);
-        numerators<MB>(s_cur, c2, acc, pb);
+  if (1 < nok) load_k_operands<D>(kaddr, SSTR % (NSLOT * SSTR), kop);
+  if (0 < nok) {
+    prepare_scores<MB, CAUSAL>(s_nx, 0 >= kmask, chunk_key(0), kstop, L, qi, h, c2, acc);
+    numerators<MB>(s_nx, c2, acc, pb);
+  }
+
+  // Barrier t of the phase sequence (t = 0 is the prologue's): group 0 runs X(k)
+  // after barrier 2k and Y(k) after 2k+1; group 1 runs one barrier later.  Odd
+  // barriers 2j+1 carry the ring protocol: before it, stage j+2 must be complete
+  // in the wave's share.  Stage j+NSLOT may overwrite stage j once barrier 2j+1
+  // has passed; each wave requests it at the start of its next MFMA phase
+  // (group 0: X(j+1), group 1: X(j)), where the issue slots are free.
+  auto odd_barrier = [&](int j) {
+    if (j + NSLOT <= nstages)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NSLOT - 3) * GPW) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  auto even_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  if (grp == 1) odd_barrier(0);
+  // The chunk loop is unrolled over the ring so that every stage offset is a
+  // compile-time immediate of the LDS instructions.
+  for (int k0 = 0; k0 < nstages; k0 += NSLOT) {
 #pragma unroll
-        for (int k = 0; k < KS; k++) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
-        }
-      } else {
-        numerators<MB>(s_cur, c2, acc, pb);
+    for (int j = 0; j < NSLOT; j++) {
+      const int k = k0 + j;
+      if (k >= nstages) break;
+      const uint32_t off1 = ((j + 1) % NSLOT) * SSTR, off2 = ((j + 2) % NSLOT) * SSTR;
+      // X(k): loads of stage k+NSLOT-1+grp, then the value product of chunk k and
+      // the scores of chunk k+1 (matrix pipe)
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const int st = k + NSLOT - 1 + grp;
+        if (st >= NSLOT && st < nstages)
+          issue_stage<D, WK>(stage_slot((j + NSLOT - 1 + grp) & (NSLOT - 1)), kbeg + st * WK * 32, sl);
       }
-      values<MB>(vop, pb, acc);
-    } else if (ok1) {
-      scores<D>(kop, qr, s_next);
+      __builtin_amdgcn_s_setprio(1);
+      if (k < nok) values<MB>(vop, pb, acc);
+      if (k + 1 < nok) scores<D>(kop, qr, s_nx);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (grp == 0) odd_barrier(k); else even_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // Y(k): operand reads for X(k+1), softmax of chunk k+1 (vector ALU).  The
+      // V reads go first; the K reads (needed one phase later) are placed after
+      // the exponentials so that they do not wait for LDS queue room in front of
+      // them.  K of a chunk past the wave's last is read too (it is not used).
+      if (k + 1 < nok) {
+        load_v_operands<D>(vaddr, off1, vop);
+        prepare_scores<MB, CAUSAL>(s_nx, k + 1 >= kmask, chunk_key(k + 1), kstop, L, qi, h, c2, acc);
+        numerators<MB>(s_nx, c2, acc, pb);
+        load_k_operands<D>(kaddr, off2, kop);
+        __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // 16 FMA + 8 exp
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the K reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // 8 exp, packs, sums
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (grp == 0) even_barrier(); else odd_barrier(k + 1);
     }
-    s_cur = s_next;
   }
+  if (grp == 0) even_barrier();
 
   // ---- merge the key groups through LDS (group 0 keeps the result).  Every wave
   //      passes every barrier; only group 0 carries on with the result.
@@ -585,20 +668,17 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
     *(float2*)(a.part_ml + ((int64_t)U * R + (prow - row0)) * 2) = make_float2(acc.mlog, lt);
 }
 
-template <int D, bool CAUSAL, int WM, int WK, int TK>
+template <int D, bool CAUSAL, int WM, int WK, int NSLOT>
 int launch_one(const AttnArgs& a, const Plan& p, hipStream_t st) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, WM, WK, TK>), dim3(p.n_units), dim3(512), 0, st,
-                     a, p);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, WM, WK, NSLOT>), dim3(p.n_units), dim3(512), 0,
+                     st, a, p);
   return (int)hipGetLastError();
 }
 
 template <bool CAUSAL>
 int launch_d128(const AttnArgs& a, const Plan& p, hipStream_t st) {
-  switch (p.variant) {
-    case kVariantR256: return launch_one<128, CAUSAL, 8, 1, 64>(a, p, st);
-    case kVariantR64: return launch_one<128, CAUSAL, 2, 4, 32>(a, p, st);
-    default: return launch_one<128, CAUSAL, 4, 2, 64>(a, p, st);  // kVariantR128
-  }
+  if (p.variant == kVariantR256) return launch_one<128, CAUSAL, 8, 1, 8>(a, p, st);
+  return launch_one<128, CAUSAL, 4, 2, 4>(a, p, st);  // kVariantR128
 }
 
 }  // namespace
@@ -608,8 +688,7 @@ int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal
   if (p.n_units == 0) return 0;
   if (head_dim == 128) return causal ? launch_d128<true>(a, p, st) : launch_d128<false>(a, p, st);
   // head_dim 64 has a single shape: 128 rows per unit
-  return causal ? launch_one<64, true, 4, 2, 64>(a, p, st)
-                : launch_one<64, false, 4, 2, 64>(a, p, st);
+  return causal ? launch_one<64, true, 4, 2, 8>(a, p, st) : launch_one<64, false, 4, 2, 8>(a, p, st);
 }
 
 }  // namespace dg

@@ -29,9 +29,9 @@ struct SeqPlan {
 
 // bf16 kernel shapes (eight waves, 32 packed rows per wave): packed rows per
 // unit = 32 x row groups; the remaining waves split the unit's keys.
-enum { kVariantR256 = 0, kVariantR128 = 1, kVariantR64 = 2, kNumVariants = 3 };
+enum { kVariantR256 = 0, kVariantR128 = 1, kNumVariants = 2 };
 constexpr int kDefaultVariant = kVariantR128;
-inline int variant_rows(int v) { return v == kVariantR256 ? 256 : (v == kVariantR64 ? 64 : 128); }
+inline int variant_rows(int v) { return v == kVariantR256 ? 256 : 128; }
 
 struct Plan {
   int32_t batch;

@@ -58,6 +58,8 @@ def _load():
         lib.dgo_partial.restype = i32
         lib.dgo_merge.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         lib.dgo_merge.restype = i32
+        lib.dgo_num_threads.argtypes = []
+        lib.dgo_num_threads.restype = i32
         _lib = lib
     return _lib
 
@@ -99,6 +101,11 @@ def _attn(fn_name, q, k_cache, v_cache, prefix_len, k_new, v_new, scale, rows):
     if rc != 0:
         raise ValueError(f"{fn_name} rejected its arguments (code {rc})")
     return out
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's row loops run on."""
+    return int(_load().dgo_num_threads())
 
 
 def canvas_attn(q, k_cache, v_cache, prefix_len, k_canvas, v_canvas, scale=None, rows=None):

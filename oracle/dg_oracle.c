@@ -34,6 +34,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -166,6 +167,9 @@ static int run(const dgo_args* a, int n_rows, const int32_t* rows, double* out) 
   }
   return failed ? -7 : 0;
 }
+
+/* Threads the parallel loops above use (the OpenMP default team size). */
+int dgo_num_threads(void) { return omp_get_max_threads(); }
 
 /* Canvas step: unmasked attention over [cache rows 0..L-1 ; canvas rows 0..Nc-1]. */
 int dgo_canvas_attn(int dtype, int B, int Nc, int Hq, int Hkv, int D, double scale,
