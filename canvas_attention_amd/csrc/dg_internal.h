@@ -27,11 +27,12 @@ struct SeqPlan {
   int32_t unit_base;   // first logical unit index of this sequence
 };
 
-// bf16 kernel shapes (eight waves, 32 packed rows per wave): packed rows per
-// unit = 32 x row groups; the remaining waves split the unit's keys.
-enum { kVariantR256 = 0, kVariantR128 = 1, kNumVariants = 2 };
+// bf16 kernel shapes.  R256 and R128: eight waves of 32 packed rows (row groups x
+// key groups, waves paired on a SIMD in ping-pong); W4: four free-running waves of
+// 64 rows; F8: eight free-running waves of 32 rows (256 rows per unit).
+enum { kVariantR256 = 0, kVariantR128 = 1, kVariantW4 = 2, kVariantF8 = 3, kNumVariants = 4 };
 constexpr int kDefaultVariant = kVariantR128;
-inline int variant_rows(int v) { return v == kVariantR256 ? 256 : 128; }
+inline int variant_rows(int v) { return v == kVariantR128 ? 128 : 256; }
 
 struct Plan {
   int32_t batch;

@@ -19,6 +19,13 @@
 namespace dg {
 namespace {
 
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  // Same dealing as the attention kernel: contiguous logical blocks on one XCD,
+  // so the rows of a kv head are merged on the XCD whose L2 holds its partials.
+  const int x = bid % kNumXcd, j = bid / kNumXcd;
+  return x * (n / kNumXcd) + min(x, n % kNumXcd) + j;
+}
+
 // Partial rows are bf16 for the bf16 path and fp32 for the fp32 path; each thread
 // combines 8 (bf16) or 4 (fp32) adjacent head_dim elements of one row.
 template <int D, bool BF16>
@@ -28,7 +35,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
   constexpr int RPB = 256 / TPR;     // rows per block
   const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = Hq / Hkv;
   const int rows_per_seq = Hkv * kCanvas * G;
-  const int64_t grow = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int64_t grow = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * RPB + threadIdx.x / TPR;
   const int dq = threadIdx.x % TPR;
   if (grow >= (int64_t)plan.batch * rows_per_seq) return;
   const int b = (int)(grow / rows_per_seq);
