@@ -54,7 +54,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t elem_size(int dtype) { return dtype == DG_BF16 ? 2 : 4; }
 
-// bf16 kernel shape for a call: DG_VARIANT=0..3 forces one for head_dim 128
+// bf16 kernel shape for a call: DG_VARIANT=0..2 forces one for head_dim 128
 // (for tuning); otherwise the default shape.  head_dim 64 has one shape.
 int bf16_variant(int head_dim) {
   if (head_dim != 128) return dg::kDefaultVariant;

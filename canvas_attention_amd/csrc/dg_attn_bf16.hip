@@ -371,19 +371,6 @@ __device__ __forceinline__ void values(const bf16x8 (&vop)[MB][2], const bf16x8 
       o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[mb][t], pb[t], o[mb], 0, 0, 0);
 }
 
-// The same product with the accumulators pinned to AGPRs (the four-wave shape
-// needs more than 256 registers; only the value accumulators, which the vector
-// ALU touches just in the rare rescale and at the end, live there).
-template <int MB>
-__device__ __forceinline__ void values_agpr(const bf16x8 (&vop)[MB][2], const bf16x8 (&pb)[2],
-                                            f32x16 (&o)[MB]) {
-#pragma unroll
-  for (int mb = 0; mb < MB; mb++)
-#pragma unroll
-    for (int t = 0; t < 2; t++)
-      asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o[mb]) : "v"(vop[mb][t]), "v"(pb[t]));
-}
-
 template <int MB>
 __device__ __forceinline__ void values(const bf16x8 (&vop)[MB][2], const bf16x8 (&pb)[2],
                                        State<MB>& acc) {
@@ -977,337 +964,6 @@ void attn_rows_kernel(AttnArgs a, Plan plan) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Four-wave shape (one wave per SIMD, two 32-row blocks per wave): the queries
-// and the value accumulators live in AGPRs, which only MFMAs touch in the loop,
-// so that the VGPRs hold the scores, operands and exponentials.  The MFMAs that
-// use AGPR operands are written as inline asm; the compiler then cannot see their
-// latency, so every place where the vector ALU reads an MFMA result (or an MFMA
-// reads a value the vector ALU has just written) carries an explicit wait.
-__device__ __forceinline__ void mfma_aq_first(f32x16& s, const bf16x8& k, const bf16x8& q) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "a"(q));
-}
-__device__ __forceinline__ void mfma_aq(f32x16& s, const bf16x8& k, const bf16x8& q) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "a"(q));
-}
-__device__ __forceinline__ void mfma_ao(f32x16& o, const bf16x8& v, const bf16x8& p) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
-}
-// Enough wait states for the result of the last issued 32x32 MFMA (16 passes) to
-// be readable by other instructions.
-__device__ __forceinline__ void xdl_result_wait() {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-}
-
-__device__ __forceinline__ float sum16(const f32x16& s) {
-  float p[4];
-#pragma unroll
-  for (int q = 0; q < 4; q++) p[q] = (s[4 * q] + s[4 * q + 1]) + (s[4 * q + 2] + s[4 * q + 3]);
-  return (p[0] + p[1]) + (p[2] + p[3]);
-}
-
-// Chunk max of both row blocks and the rare rescale; the accumulators are read
-// only after the wait for the value MFMAs of the previous chunk.
-template <int MB, bool CAUSAL>
-__device__ __forceinline__ void prepare_scores_w4(f32x16 (&s)[2], bool masked, int key0, int kstop,
-                                                  int L, const int (&qi)[2], int h, float c2,
-                                                  StateN<2, MB>& acc) {
-  if (masked) {
-#pragma unroll
-    for (int rb = 0; rb < 2; rb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int key = key0 + 8 * (i / 4) + 4 * h + (i % 4);
-        bool ok = key < kstop;
-        if (CAUSAL) ok = ok && (key < L || key - L <= qi[rb]);
-        s[rb][i] = ok ? s[rb][i] : -INFINITY;
-      }
-  }
-  float cm[2];
-  bool rise = false;
-#pragma unroll
-  for (int rb = 0; rb < 2; rb++) {
-    float m = s[rb][0];
-#pragma unroll
-    for (int i = 1; i < 16; i++) m = fmaxf(m, s[rb][i]);
-    cm[rb] = m * c2;
-    rise = rise || cm[rb] > acc.mlog[rb] + kRescaleThreshold;
-  }
-  if (__any(rise)) {
-    xdl_result_wait();
-#pragma unroll
-    for (int rb = 0; rb < 2; rb++) {
-      const float mnew = fmaxf(acc.mlog[rb], partner_max(cm[rb]));
-      const float alpha = __builtin_amdgcn_exp2f(acc.mlog[rb] - mnew);
-      acc.mlog[rb] = mnew;
-      acc.lsum[rb] *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < MB; mb++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc.o[rb][mb][i] *= alpha;
-    }
-  }
-}
-
-template <int D, bool CAUSAL, int NSLOT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_w4_kernel(AttnArgs a, Plan plan) {
-  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-  constexpr int NB = 2, NW = 4, NT = 256, R = 256;
-  constexpr int KS = D / 16, CH = D / 8, MB = D / 32, ROWB = D * 2, TILEB = 32 * ROWB;
-  constexpr int SSTR = TILEB;                   // one 32-key tile per stage
-  constexpr int GPW = 2 * TILEB / 1024 / NW;    // global_load_lds per wave per stage
-  static_assert(GPW >= 1, "stage load split");
-  static_assert((NSLOT & (NSLOT - 1)) == 0 && NSLOT >= 4, "ring of 4, 8, ... stages");
-  static_assert(NSLOT * SSTR <= kVRegion, "K and V regions of the ring");
-  __shared__ __attribute__((aligned(1024))) char ring[kVRegion + NSLOT * SSTR];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int n = lane & 31, h = lane >> 5;
-  const int U = xcd_remap(blockIdx.x, gridDim.x);
-  const Unit u = decode_unit(plan, U);
-  const SeqPlan sp = plan.seq[u.b];
-  const int L = sp.prefix_len;
-  const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = Hq / Hkv;
-  const int row0 = u.rt * R;
-  int kend = L + kCanvas;
-  if (CAUSAL) kend = min(kend, L + (row0 + R - 1) / G + 1);
-  const int kbeg = u.s * sp.split_keys;
-  const int kstop = min(kbeg + sp.split_keys, kend);
-  const int nstages = kstop > kbeg ? (kstop - kbeg + 31) / 32 : 0;
-
-  const int64_t cap = a.cap;
-  const uint16_t* kc = (const uint16_t*)a.k_cache;
-  const uint16_t* vc = (const uint16_t*)a.v_cache;
-  const uint16_t* kn = (const uint16_t*)a.k_new;
-  const uint16_t* vn = (const uint16_t*)a.v_new;
-
-  // ---- commit: append the block's K/V rows of head g to cache rows L..L+255
-  if (CAUSAL && a.k_append != nullptr) {
-    const int cnt = sp.n_splits * plan.n_rowtiles;
-    const int w = u.s * plan.n_rowtiles + u.rt;
-    const int rpu = (kCanvas + cnt - 1) / cnt;
-    const int r0 = min(kCanvas, w * rpu), r1 = min(kCanvas, r0 + rpu);
-    const int per = (r1 - r0) * CH;
-    for (int idx = tid; idx < 2 * per; idx += NT) {
-      const int which = idx / per, rem = idx % per;
-      const int r = r0 + rem / CH, c = rem % CH;
-      const int64_t src = ((int64_t)(u.b * kCanvas + r) * Hkv + u.g) * D + c * 8;
-      const int64_t dst = (((int64_t)u.b * cap + L + r) * Hkv + u.g) * D + c * 8;
-      const uint4 val = *(const uint4*)((which ? vn : kn) + src);
-      *(uint4*)((uint16_t*)(which ? a.v_append : a.k_append) + dst) = val;
-    }
-  }
-
-  // ---- queries of the wave's row blocks (B operands of S^T = K Q^T)
-  bf16x8 qa[NB][KS];  // used only as AGPR operands of the score MFMAs
-  int qi[NB];
-#pragma unroll
-  for (int rb = 0; rb < NB; rb++) {
-    const int prow = row0 + 32 * NB * wave + 32 * rb + n;
-    qi[rb] = prow / G;
-    const uint16_t* qp = (const uint16_t*)a.q +
-                         ((int64_t)(u.b * kCanvas + qi[rb]) * Hq + u.g * G + prow % G) * D + (D / 2) * h;
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) qa[rb][ks] = *(const bf16x8*)(qp + 8 * ks);
-  }
-
-  StageLoads<D, 1, NW> sl;
-  stage_loads_init<D, 1, NW>(sl, (const char*)(kc + ((int64_t)u.b * cap * Hkv + u.g) * D),
-                             (const char*)(vc + ((int64_t)u.b * cap * Hkv + u.g) * D),
-                             (const char*)(kn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
-                             (const char*)(vn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
-                             Hkv * D * 2, L, kstop, wave, lane);
-  const LaneOffsets<D> lo = lane_offsets<D>(lane);
-  const int wave_qi_min = (row0 + 32 * NB * wave) / G;
-  const int wave_qi_max = (row0 + 32 * NB * wave + 32 * NB - 1) / G;
-  const float c2 = a.scale_log2;
-  // chunks with visible keys for this wave: k < nok; chunks needing masks: k >= kmask
-  const int klimit = CAUSAL ? min(kstop, L + wave_qi_max + 1) : kstop;
-  const int nok = klimit > kbeg ? (klimit - kbeg + 31) / 32 : 0;
-  int kmask = (kstop - kbeg) / 32;
-  if (CAUSAL) {
-    const int x = wave_qi_min + L - 31 - kbeg;
-    kmask = min(kmask, x >= 0 ? x / 32 + 1 : 0);
-  }
-
-  StateN<NB, MB> acc;
-#pragma unroll
-  for (int rb = 0; rb < NB; rb++) {
-#pragma unroll
-    for (int mb = 0; mb < MB; mb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) acc.o[rb][mb][i] = 0.f;
-    acc.mlog[rb] = -1e30f;
-    acc.lsum[rb] = 0.f;
-  }
-
-  const uint32_t lring = lds_addr(ring);
-  uint32_t kaddr[KS], vaddr[MB];
-#pragma unroll
-  for (int ks = 0; ks < KS; ks++) kaddr[ks] = lring + lo.k[ks];
-#pragma unroll
-  for (int mb = 0; mb < MB; mb++) vaddr[mb] = lring + kVRegion + lo.v[mb];
-
-  // ---- ring protocol (barrier B(k) ends chunk k): a wave reads K(j) in chunk j-2
-  //      and V(j) in chunk j-1 and consumes V(j) in chunk j, so stage j is free
-  //      after B(j) and stage j+NSLOT is requested then; K(j) needs stage j
-  //      complete, so before B(j-3) each wave waits for its own loads of it.
-  const int npre = min(NSLOT, nstages);
-  for (int st = 0; st < npre; st++)
-    issue_stage<D, 1, NW>(lring + (uint32_t)(st & (NSLOT - 1)) * SSTR, kbeg + st * 32, sl);
-  if (nstages >= NSLOT)
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSLOT - 3) * GPW) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-  for (int rb = 0; rb < NB; rb++)
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) asm volatile("" ::"a"(qa[rb][ks]));
-
-  f32x16 sc[NB];       // scores of the chunk whose softmax runs next
-  bf16x8 kop[KS];      // K operands of the next score MFMAs
-  bf16x8 vop[MB][2];   // V^T operands of the next value MFMAs
-  bf16x8 pb[NB][2];    // packed exponentials of the row blocks
-  if (0 < nok) {
-    load_k_operands<D>(kaddr, 0, kop);
-#pragma unroll
-    for (int rb = 0; rb < NB; rb++) {
-      mfma_aq_first(sc[rb], kop[0], qa[rb][0]);
-#pragma unroll
-      for (int ks = 1; ks < KS; ks++) mfma_aq(sc[rb], kop[ks], qa[rb][ks]);
-    }
-    load_v_operands<D>(vaddr, 0, vop);
-    xdl_result_wait();
-  }
-  if (1 < nok) load_k_operands<D>(kaddr, SSTR, kop);
-
-  for (int k0 = 0; k0 < nstages; k0 += NSLOT) {
-#pragma unroll
-    for (int j = 0; j < NSLOT; j++) {
-      const int k = k0 + j;
-      if (k >= nstages) break;
-      const uint32_t off1 = ((j + 1) % NSLOT) * SSTR, off2 = ((j + 2) % NSLOT) * SSTR;
-      f32x16 sn[NB];
-      if (k < nok) {
-        prepare_scores_w4<MB, CAUSAL>(sc, k >= kmask, kbeg + 32 * k, kstop, L, qi, h, c2, acc);
-        const float nm0 = -acc.mlog[0], nm1 = -acc.mlog[1];
-        constexpr int EPS = 32 / (2 * KS);  // exponentials per score MFMA
-        if (k + 1 < nok) {
-          // group A: the 2*KS score MFMAs of chunk k+1 between the exponentials of chunk k
-#pragma unroll
-          for (int i = 0; i < 2 * KS; i++) {
-            const int rb = i & 1, ks = i >> 1;
-            if (ks == 0) mfma_aq_first(sn[rb], kop[0], qa[rb][0]);
-            else mfma_aq(sn[rb], kop[ks], qa[rb][ks]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int e = 0; e < EPS; e++) {
-              const int idx = i * EPS + e, b2 = idx / 16, el = idx % 16;
-              sc[b2][el] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b2][el], c2, b2 ? nm1 : nm0));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        } else {
-#pragma unroll
-          for (int idx = 0; idx < 32; idx++) {
-            const int b2 = idx / 16, el = idx % 16;
-            sc[b2][el] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b2][el], c2, b2 ? nm1 : nm0));
-          }
-        }
-        // block 0 packed for its value MFMAs; its row sum
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-#pragma unroll
-          for (int j = 0; j < 8; j++) pb[0][t][j] = (__bf16)sc[0][8 * t + j];
-        acc.lsum[0] += sum16(sc[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_nop 2" ::: "memory");
-        // group B: value MFMAs of block 0 between the pack and sum of block 1
-#pragma unroll
-        for (int i = 0; i < 2 * MB; i++) {
-          const int t = i / MB, mb = i % MB;
-          mfma_ao(acc.o[0][mb], vop[mb][t], pb[0][t]);
-          __builtin_amdgcn_sched_barrier(0);
-          if (i < 2) {
-#pragma unroll
-            for (int j = 0; j < 8; j++) pb[1][i][j] = (__bf16)sc[1][8 * i + j];
-          } else if (i == 2) {
-            acc.lsum[1] += sum16(sc[1]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // group C: value MFMAs of block 1 between the K operand reads of chunk k+2
-        // (read even past the wave's last chunk: unused)
-#pragma unroll
-        for (int i = 0; i < 2 * MB; i++) {
-          const int t = i / MB, mb = i % MB;
-          mfma_ao(acc.o[1][mb], vop[mb][t], pb[1][t]);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int ks = i * KS / (2 * MB); ks < (i + 1) * KS / (2 * MB); ks++)
-            kop[ks] = *(const LDS_AS bf16x8*)(uintptr_t)(kaddr[ks] + off2);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (k + 1 < nok) load_v_operands<D>(vaddr, off1, vop);
-      }
-#pragma unroll
-      for (int rb = 0; rb < NB; rb++) sc[rb] = sn[rb];
-      // ---- barrier B(k): stage k+3 complete in every wave's share
-      if (k + NSLOT <= nstages)
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSLOT - 4) * GPW) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      if (k + NSLOT < nstages)
-        issue_stage<D, 1, NW>(lring + (uint32_t)j * SSTR, kbeg + (k + NSLOT) * 32, sl);
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  xdl_result_wait();
-  // ---- write both row blocks (as the eight-wave kernel does, one block at a time
-  //      through the wave's LDS staging area)
-  const bool direct = sp.n_splits == 1;
-  constexpr int SROWB = 64 * 2 + 16;
-  char* stage = ring + wave * 32 * SROWB;
-  const int r_lo = lane / 8, cq = lane % 8;
-#pragma unroll
-  for (int rb = 0; rb < NB; rb++) {
-    const float lt = partner_sum(acc.lsum[rb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* rowp[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; kk++) {
-      const int p = row0 + 32 * NB * wave + 32 * rb + 8 * kk + r_lo;
-      rowp[kk] = direct ? (uint16_t*)a.out +
-                              ((int64_t)(u.b * kCanvas + p / G) * Hq + u.g * G + p % G) * D
-                        : (uint16_t*)a.part_o + ((int64_t)U * R + (p - row0)) * D;
-    }
-#pragma unroll
-    for (int half = 0; half < MB / 2; half++) {
-#pragma unroll
-      for (int mbl = 0; mbl < 2; mbl++)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-          typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4e;
-          bf16x4e v;
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) v[jj] = (__bf16)(acc.o[rb][2 * half + mbl][4 * q4 + jj] * inv);
-          *(bf16x4e*)(stage + n * SROWB + (32 * mbl + 8 * q4 + 4 * h) * 2) = v;
-        }
-#pragma unroll
-      for (int kk = 0; kk < 4; kk++)
-        *(uint4*)(rowp[kk] + 64 * half + 8 * cq) =
-            *(const uint4*)(stage + (8 * kk + r_lo) * SROWB + 16 * cq);
-    }
-    if (!direct && h == 0) {
-      const int prow = row0 + 32 * NB * wave + 32 * rb + n;
-      *(float2*)(a.part_ml + ((int64_t)U * R + (prow - row0)) * 2) = make_float2(acc.mlog[rb], lt);
-    }
-  }
-}
-
 template <int D, bool CAUSAL, int WM, int WK, int NSLOT>
 int launch_one(const AttnArgs& a, const Plan& p, hipStream_t st) {
   hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, WM, WK, NSLOT>), dim3(p.n_units), dim3(512), 0,
@@ -1325,10 +981,6 @@ int launch_rows(const AttnArgs& a, const Plan& p, hipStream_t st) {
 template <bool CAUSAL>
 int launch_d128(const AttnArgs& a, const Plan& p, hipStream_t st) {
   if (p.variant == kVariantR256) return launch_one<128, CAUSAL, 8, 1, 8>(a, p, st);
-  if (p.variant == kVariantW4) {
-    hipLaunchKernelGGL((attn_w4_kernel<128, CAUSAL, 8>), dim3(p.n_units), dim3(256), 0, st, a, p);
-    return (int)hipGetLastError();
-  }
   if (p.variant == kVariantF8) return launch_rows<128, CAUSAL, 1, 8>(a, p, st);
   return launch_one<128, CAUSAL, 4, 2, 4>(a, p, st);  // kVariantR128
 }

@@ -28,9 +28,9 @@ struct SeqPlan {
 };
 
 // bf16 kernel shapes.  R256 and R128: eight waves of 32 packed rows (row groups x
-// key groups, waves paired on a SIMD in ping-pong); W4: four free-running waves of
-// 64 rows; F8: eight free-running waves of 32 rows (256 rows per unit).
-enum { kVariantR256 = 0, kVariantR128 = 1, kVariantW4 = 2, kVariantF8 = 3, kNumVariants = 4 };
+// key groups, waves paired on a SIMD in ping-pong); F8: eight free-running waves
+// of 32 rows (256 rows per unit).
+enum { kVariantR256 = 0, kVariantR128 = 1, kVariantF8 = 2, kNumVariants = 3 };
 constexpr int kDefaultVariant = kVariantR128;
 inline int variant_rows(int v) { return v == kVariantR128 ? 128 : 256; }
 
