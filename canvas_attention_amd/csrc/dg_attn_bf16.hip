@@ -116,17 +116,14 @@ struct State {
   float lsum;    // sum of this lane's exponentials (the partner lane holds the rest)
 };
 
-// One global_load_lds_dwordx4: every lane copies 16 bytes from its global address
-// into LDS at m0 + 16*lane.  Issued from inline asm so that the compiler does not
-// see an LDS write it cannot disambiguate from the operand reads of the other
-// ring slot (it would otherwise drain every prefetch before the first of them);
-// completion is tracked explicitly with s_waitcnt vmcnt before each stage's
-// barrier.  Nothing else in the kernel uses m0.
-__device__ __forceinline__ void gll_saddr(const char* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(lds)
-               : "memory");
-}
+// global_load_lds_dwordx4: every lane copies 16 bytes from its global address
+// into LDS at m0 + instruction offset + 16*lane.  Issued from inline asm so that
+// the compiler does not see an LDS write it cannot disambiguate from the operand
+// reads of the other ring slots (it would otherwise drain every prefetch before
+// the first of them); completion is tracked explicitly with s_waitcnt vmcnt
+// before each stage's barrier.  The single-source form is written out in
+// issue_stage; this is the per-lane-address form.  Nothing else in the kernel
+// uses m0 (the compiler reserves it and takes no clobber of it).
 __device__ __forceinline__ void gll_vaddr(const char* vaddr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vaddr), "s"(lds)
                : "memory");
@@ -145,15 +142,23 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-// This wave's share of the global_load_lds instructions that fill one ring stage:
-// for every key group kt a 32-key tile, K rows then V rows.  Each instruction
-// moves 1 KB: lane l writes 16 bytes at dst + 16*l, i.e. tile row l / CH of the
-// instruction's row block, physical chunk l % CH, and fetches the logical chunk
-// that the swizzle stores there (K: chunk ^ (row % CH); V: chunk ^ 4*(row % 4)).
-// Everything that does not depend on the stage is computed once per wave; per
-// stage only the byte offset of its first key is formed, and a stage lying
-// wholly in the cache or wholly in the canvas (every stage but the one at the
-// seam and the unit's last) is issued as scalar base + 32-bit lane offset.
+// This wave's share of the global_load_lds instructions that fill one ring stage.
+// A stage holds, for every key group kt, a 32-key K tile and a 32-key V tile; the
+// K tiles of the stage are consecutive in LDS and so are its V tiles, so each
+// half is a run of 1 KB blocks (block b: keys b*RPI .. b*RPI+RPI-1 of the stage).
+// Waves 0 .. NW/2-1 fill the K half and the others the V half, each GPW
+// consecutive blocks: one M0 value serves all of a wave's loads, which differ
+// only in the instruction offset 1024e (the offset moves the LDS destination and
+// the global address alike; the lane offsets take it back out of the latter).
+// Writing M0 before every load would stall the wave at each of them.
+// Each load moves 1 KB: lane l writes 16 bytes at 16*l of its block, i.e. block
+// row l / CH, physical chunk l % CH, and fetches the logical chunk that the
+// swizzle stores there (K: chunk ^ (row % CH); V: chunk ^ 4*(row % 4), row
+// within the tile).  Everything that does not depend on the stage is computed
+// once per wave; per stage only the byte offset of its first key is formed, and
+// a stage lying wholly in the cache or wholly in the canvas (every stage but the
+// one at the seam and the unit's last) is issued as scalar base + 32-bit lane
+// offsets.
 // The ring holds the K tiles of every stage in its first 64 KB and the V tiles in
 // the second: stage s, key group kt at s*WK*TILEB + kt*TILEB (+ kVRegion for V),
 // so that every operand read is a per-lane base plus an immediate offset.
@@ -163,13 +168,14 @@ template <int D, int WK, int NW = 8>
 struct StageLoads {
   static constexpr int CH = D / 8, ROWB = D * 2, RPI = 1024 / ROWB, IPT = 32 / RPI;
   static constexpr int TILEB = 32 * ROWB, GPW = WK * 2 * IPT / NW;
-  uint64_t cb[GPW];         // cache K or V base of (sequence, kv head) for instruction e
-  uint64_t nb[GPW];         // canvas/block K or V base minus L rows for instruction e
-  uint32_t rowoff[GPW];     // (kt*32 + first row) * row stride of instruction e
-  uint32_t dst[GPW];        // LDS offset of instruction e within a stage
-  uint32_t lane[GPW];       // lane byte offset: row (lane / CH) * stride + swizzled chunk
-  int32_t krow[GPW];        // lane's key offset within the stage (kt*32 + row)
-  uint32_t lrs;             // (lane / CH) * row stride
+  static_assert(NW % 2 == 0 && GPW * NW == WK * 2 * IPT && GPW >= 1 && GPW <= 4,
+                "whole blocks per wave, instruction offsets below 4 KB");
+  uint64_t cb;              // cache K or V base of (sequence, kv head)
+  uint64_t nb;              // canvas/block K or V base minus L rows
+  uint32_t rowoff;          // first row of the wave's blocks * row stride
+  uint32_t dst;             // LDS offset of the wave's first block within a stage
+  uint32_t lane[GPW];       // lane byte offset of load e (row, swizzled chunk) less 1024e
+  int32_t krow;             // lane's key offset within the stage in load 0 (+RPI per load)
   int32_t rsb, L, kstop;
 };
 
@@ -182,26 +188,34 @@ __device__ __forceinline__ void stage_loads_init(StageLoads<D, WK, NW>& sl, cons
   sl.rsb = rsb;
   sl.L = L;
   sl.kstop = kstop;
-  sl.lrs = (uint32_t)lr * (uint32_t)rsb;
+  const bool isv = wave >= NW / 2;  // wave-uniform
+  const int b0 = (wave % (NW / 2)) * SL::GPW;
   const uint64_t ukc = (uint64_t)(uintptr_t)kc, uvc = (uint64_t)(uintptr_t)vc;
   const uint64_t ukn = (uint64_t)(uintptr_t)kn - (uint64_t)L * (uint64_t)rsb;
   const uint64_t uvn = (uint64_t)(uintptr_t)vn - (uint64_t)L * (uint64_t)rsb;
+  sl.cb = uniform64(isv ? uvc : ukc);
+  sl.nb = uniform64(isv ? uvn : ukn);
+  sl.rowoff = (uint32_t)(b0 * SL::RPI * rsb);
+  sl.dst = (uint32_t)((isv ? kVRegion : 0) + b0 * 1024);
+  sl.krow = b0 * SL::RPI + lr;
 #pragma unroll
   for (int e = 0; e < SL::GPW; e++) {
-    const int instr = wave + NW * e;  // wave-uniform
-    const int kt = instr / (2 * SL::IPT), w2 = instr % (2 * SL::IPT);
-    const bool isv = w2 >= SL::IPT;
-    const int ri = w2 % SL::IPT;
-    const int r0 = ri * SL::RPI;
-    sl.cb[e] = uniform64(isv ? uvc : ukc);
-    sl.nb[e] = uniform64(isv ? uvn : ukn);
-    sl.rowoff[e] = (uint32_t)((kt * 32 + r0) * rsb);
-    sl.dst[e] = (uint32_t)((isv ? kVRegion : 0) + kt * SL::TILEB + ri * 1024);
-    const int r = r0 + lr;
+    const int r = ((b0 + e) % SL::IPT) * SL::RPI + lr;  // row within the tile
     const int sw = isv ? ((4 * (r & 3)) & (SL::CH - 1)) : (r & (SL::CH - 1));
-    sl.lane[e] = (uint32_t)lr * (uint32_t)rsb + 16u * (uint32_t)(lp ^ sw);
-    sl.krow[e] = kt * 32 + r;
+    sl.lane[e] = (uint32_t)(e * SL::RPI + lr) * (uint32_t)rsb + 16u * (uint32_t)(lp ^ sw) -
+                 1024u * (uint32_t)e;
   }
+}
+
+// Where the keys of the stage from skey0 come from: 1 wholly the cache, 2 wholly
+// the canvas (both issued as scalar base + lane offsets), 0 both or past the
+// unit's end (rows formed per lane).
+template <int D, int WK, int NW>
+__device__ __forceinline__ int stage_source(int skey0, const StageLoads<D, WK, NW>& sl) {
+  const int send = skey0 + 32 * WK;
+  if (send <= sl.L && send <= sl.kstop) return 1;
+  if (skey0 >= sl.L && send <= sl.kstop) return 2;
+  return 0;
 }
 
 // Issues the wave's loads of one stage (keys from skey0, WK tiles) into the LDS
@@ -211,26 +225,42 @@ __device__ __forceinline__ void stage_loads_init(StageLoads<D, WK, NW>& sl, cons
 template <int D, int WK, int NW>
 __device__ __forceinline__ void issue_stage(uint32_t slot, int skey0, const StageLoads<D, WK, NW>& sl) {
   using SL = StageLoads<D, WK, NW>;
-  const int send = skey0 + 32 * WK;
-  const bool in_cache = send <= sl.L && send <= sl.kstop;
-  const bool in_canvas = skey0 >= sl.L && send <= sl.kstop;
-  if (in_cache || in_canvas) {
-    const uint64_t koff = (uint64_t)(int64_t)skey0 * (uint64_t)sl.rsb;
-#pragma unroll
-    for (int e = 0; e < SL::GPW; e++) {
-      const uint64_t tb = (in_cache ? sl.cb[e] : sl.nb[e]) + koff + sl.rowoff[e];
-      gll_saddr(uniform_ptr((const char*)(uintptr_t)tb), sl.lane[e],
-                __builtin_amdgcn_readfirstlane(slot + sl.dst[e]));
-    }
+  constexpr int G = SL::GPW;
+  const int src = stage_source(skey0, sl);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + sl.dst);
+  if (src > 0) {
+    const uint64_t tb = (src == 1 ? sl.cb : sl.nb) + (uint64_t)(int64_t)skey0 * (uint64_t)sl.rsb + sl.rowoff;
+    const char* sb = uniform_ptr((const char*)(uintptr_t)tb);
+    if constexpr (G == 1)
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
+                   ::"v"(sl.lane[0]), "s"(m0), "s"(sb) : "memory");
+    else if constexpr (G == 2)
+      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %3\n\t"
+                   "global_load_lds_dwordx4 %1, %3 offset:1024"
+                   ::"v"(sl.lane[0]), "v"(sl.lane[1]), "s"(m0), "s"(sb) : "memory");
+    else if constexpr (G == 3)
+      asm volatile("s_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %0, %4\n\t"
+                   "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
+                   "global_load_lds_dwordx4 %2, %4 offset:2048"
+                   ::"v"(sl.lane[0]), "v"(sl.lane[1]), "v"(sl.lane[2]), "s"(m0), "s"(sb)
+                   : "memory");
+    else
+      asm volatile("s_mov_b32 m0, %4\n\tglobal_load_lds_dwordx4 %0, %5\n\t"
+                   "global_load_lds_dwordx4 %1, %5 offset:1024\n\t"
+                   "global_load_lds_dwordx4 %2, %5 offset:2048\n\t"
+                   "global_load_lds_dwordx4 %3, %5 offset:3072"
+                   ::"v"(sl.lane[0]), "v"(sl.lane[1]), "v"(sl.lane[2]), "v"(sl.lane[3]),
+                     "s"(m0), "s"(sb) : "memory");
   } else {
 #pragma unroll
-    for (int e = 0; e < SL::GPW; e++) {
-      const int key = min(skey0 + sl.krow[e], sl.kstop - 1);
-      const uint64_t base = key < sl.L ? sl.cb[e] : sl.nb[e];
+    for (int e = 0; e < G; e++) {
+      const int key = min(skey0 + sl.krow + e * SL::RPI, sl.kstop - 1);
+      const uint64_t base = key < sl.L ? sl.cb : sl.nb;
       const uint64_t row = base + (uint64_t)(int64_t)key * (uint64_t)sl.rsb;
       // the row is the lane's own here: keep only the swizzled chunk of the lane offset
-      gll_vaddr((const char*)(uintptr_t)(row + (sl.lane[e] - sl.lrs)),
-                __builtin_amdgcn_readfirstlane(slot + sl.dst[e]));
+      const uint32_t chunk = sl.lane[e] + 1024u * (uint32_t)e -
+                             (uint32_t)(sl.krow - (sl.krow / SL::RPI) * SL::RPI + e * SL::RPI) * (uint32_t)sl.rsb;
+      gll_vaddr((const char*)(uintptr_t)(row + chunk), m0 + 1024u * (uint32_t)e);
     }
   }
 }
