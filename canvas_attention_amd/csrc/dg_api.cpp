@@ -128,6 +128,9 @@ void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
   p->variant = variant;
   p->n_rowtiles = NRT;
   p->rows_per_unit = R;
+  p->g = G;
+  p->rcp_g = dg::rcp_u32((uint32_t)G);
+  p->rcp_nrt = dg::rcp_u32((uint32_t)NRT);
   int units = 0;
   for (int b = 0; b < s->batch; b++) {
     const int64_t K = (int64_t)prefix_len[b] + dg::kCanvas;
@@ -139,6 +142,8 @@ void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
     p->seq[b].n_splits = S;
     p->seq[b].split_keys = (int)sk;
     p->seq[b].unit_base = units;
+    p->seq[b].rcp_s = dg::rcp_u32((uint32_t)S);
+    p->seq[b].rcp_snrt = dg::rcp_u32((uint32_t)(S * NRT));
     units += S * per_split;
   }
   p->n_units = units;
@@ -223,6 +228,10 @@ dg_status prepare(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
   c->shape = *shape;
   c->causal = commit;
   make_plan(shape, prefix_len, &c->plan);
+  // unit and row indices stay below 2^16, which keeps every kernel division n/d with
+  // n*d < 2^32 (the reciprocal-multiplier form is exact there)
+  if (c->plan.n_units >= dg::kMaxUnits)
+    return fail(DG_ERR_SHAPE, "%d work units, at most %d", c->plan.n_units, dg::kMaxUnits - 1);
   const size_t need_ws = plan_workspace(shape, c->plan);
   if (need_ws > ws_bytes)
     return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes, this call needs %zu", ws_bytes, need_ws);

@@ -78,17 +78,30 @@ struct Unit {
   int b, g, s, rt;
 };
 
-__device__ __forceinline__ Unit decode_unit(const Plan& p, int U) {
+// floor(n / d) from the host's reciprocal multiplier m = rcp_u32(d), valid for n*d < 2^32
+// (m = 0 encodes d = 1); written without a branch so that the scalar loads around it
+// stay in one basic block and are issued together
+__device__ __forceinline__ int div_rcp(int n, uint32_t m) {
+  return (int)__umulhi((uint32_t)n, m) + (m == 0u ? n : 0);
+}
+
+// Unit U of the launch and the plan of its sequence.  Sequence 0's entry is read
+// together with the plan header; a unit of a later sequence costs one more scalar
+// round trip.
+__device__ __forceinline__ Unit decode_unit(const Plan& p, int U, SeqPlan& sp) {
+  sp = p.seq[0];
   int b = 0;
   for (int i = 1; i < p.batch; i++)
     if (U >= p.seq[i].unit_base) b = i;
-  const int local = U - p.seq[b].unit_base;
-  const int S = p.seq[b].n_splits, NRT = p.n_rowtiles;
+  if (b != 0) sp = p.seq[b];
+  const int local = U - sp.unit_base;
+  const int S = sp.n_splits, NRT = p.n_rowtiles;
+  const int q = div_rcp(local, p.rcp_nrt);  // local / NRT
   Unit u;
   u.b = b;
-  u.g = local / (S * NRT);
-  u.s = (local / NRT) % S;
-  u.rt = local % NRT;
+  u.g = div_rcp(local, sp.rcp_snrt);
+  u.s = q - div_rcp(q, sp.rcp_s) * S;
+  u.rt = local - q * NRT;
   return u;
 }
 
@@ -218,6 +231,31 @@ __device__ __forceinline__ int stage_source(int skey0, const StageLoads<D, WK, N
   return 0;
 }
 
+// NL (1..4) global_load_lds_dwordx4 from scalar base sb + lane offset vo[e] + 1024e
+// into LDS at m0 + 1024e + 16*lane: one m0 write serves the whole block.
+template <int NL>
+__device__ __forceinline__ void gll_block(const char* sb, const uint32_t* vo, uint32_t m0) {
+  static_assert(NL >= 1 && NL <= 4, "instruction offsets below 4 KB");
+  if constexpr (NL == 1)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
+                 ::"v"(vo[0]), "s"(m0), "s"(sb) : "memory");
+  else if constexpr (NL == 2)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %3\n\t"
+                 "global_load_lds_dwordx4 %1, %3 offset:1024"
+                 ::"v"(vo[0]), "v"(vo[1]), "s"(m0), "s"(sb) : "memory");
+  else if constexpr (NL == 3)
+    asm volatile("s_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %0, %4\n\t"
+                 "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %2, %4 offset:2048"
+                 ::"v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "s"(m0), "s"(sb) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %4\n\tglobal_load_lds_dwordx4 %0, %5\n\t"
+                 "global_load_lds_dwordx4 %1, %5 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %2, %5 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %3, %5 offset:3072"
+                 ::"v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(m0), "s"(sb) : "memory");
+}
+
 // Issues the wave's loads of one stage (keys from skey0, WK tiles) into the LDS
 // slot.  Tiles past the unit's last key are loaded too (rows clamped onto the
 // unit's last key) so that each wave always has the same number of loads per
@@ -230,27 +268,7 @@ __device__ __forceinline__ void issue_stage(uint32_t slot, int skey0, const Stag
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + sl.dst);
   if (src > 0) {
     const uint64_t tb = (src == 1 ? sl.cb : sl.nb) + (uint64_t)(int64_t)skey0 * (uint64_t)sl.rsb + sl.rowoff;
-    const char* sb = uniform_ptr((const char*)(uintptr_t)tb);
-    if constexpr (G == 1)
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
-                   ::"v"(sl.lane[0]), "s"(m0), "s"(sb) : "memory");
-    else if constexpr (G == 2)
-      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %3\n\t"
-                   "global_load_lds_dwordx4 %1, %3 offset:1024"
-                   ::"v"(sl.lane[0]), "v"(sl.lane[1]), "s"(m0), "s"(sb) : "memory");
-    else if constexpr (G == 3)
-      asm volatile("s_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %0, %4\n\t"
-                   "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
-                   "global_load_lds_dwordx4 %2, %4 offset:2048"
-                   ::"v"(sl.lane[0]), "v"(sl.lane[1]), "v"(sl.lane[2]), "s"(m0), "s"(sb)
-                   : "memory");
-    else
-      asm volatile("s_mov_b32 m0, %4\n\tglobal_load_lds_dwordx4 %0, %5\n\t"
-                   "global_load_lds_dwordx4 %1, %5 offset:1024\n\t"
-                   "global_load_lds_dwordx4 %2, %5 offset:2048\n\t"
-                   "global_load_lds_dwordx4 %3, %5 offset:3072"
-                   ::"v"(sl.lane[0]), "v"(sl.lane[1]), "v"(sl.lane[2]), "v"(sl.lane[3]),
-                     "s"(m0), "s"(sb) : "memory");
+    gll_block<G>(uniform_ptr((const char*)(uintptr_t)tb), sl.lane, m0);
   } else {
 #pragma unroll
     for (int e = 0; e < G; e++) {
@@ -446,13 +464,13 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
   const int n = lane & 31, h = lane >> 5;
   const int rg = wave % WM, kg = wave / WM;
   const int U = xcd_remap(blockIdx.x, gridDim.x);
-  const Unit u = decode_unit(plan, U);
-  const SeqPlan sp = plan.seq[u.b];
+  SeqPlan sp;
+  const Unit u = decode_unit(plan, U, sp);
   const int L = sp.prefix_len;
-  const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = Hq / Hkv;
+  const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = plan.g;
   const int row0 = u.rt * R;
   int kend = L + kCanvas;
-  if (CAUSAL) kend = min(kend, L + (row0 + R - 1) / G + 1);
+  if (CAUSAL) kend = min(kend, L + div_rcp(row0 + R - 1, plan.rcp_g) + 1);
   const int kbeg = u.s * sp.split_keys;
   const int kstop = min(kbeg + sp.split_keys, kend);
   const int ntiles = kstop > kbeg ? (kstop - kbeg + 31) / 32 : 0;
@@ -481,19 +499,8 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
     }
   }
 
-  // ---- queries of this wave: B operand of S^T = K Q^T, lane (n, h) holds
-  //      q[row][D/2*h + 8*ks .. +8] for k-step ks (a fixed permutation of head_dim
-  //      shared with the K operand)
-  bf16x8 qr[KS];
-  const int prow = row0 + 32 * rg + n;
-  const int qi = prow / G;
-  {
-    const int hh = prow % G;
-    const uint16_t* qp = (const uint16_t*)a.q +
-                         ((int64_t)(u.b * kCanvas + qi) * Hq + u.g * G + hh) * D + (D / 2) * h;
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) qr[ks] = *(const bf16x8*)(qp + 8 * ks);
-  }
+  const int prow = row0 + 32 * rg + n;  // packed row of this lane's scores
+  const int qi = div_rcp(prow, plan.rcp_g);
 
   StageLoads<D, WK, 8> sl;
   stage_loads_init<D, WK, 8>(sl, (const char*)(kc + ((int64_t)u.b * cap * Hkv + u.g) * D),
@@ -501,9 +508,54 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
                           (const char*)(kn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
                           (const char*)(vn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
                           Hkv * D * 2, L, kstop, wave, lane);
+  // The first two stages (the operands of the first chunk and the scores of the
+  // second) are requested as soon as the unit is known; everything below overlaps
+  // their flight.  Only these two precede the first wait: the compiler's wait for
+  // the query registers also covers every load issued before it.
+  static_assert((NSLOT & (NSLOT - 1)) == 0, "ring of a power-of-two number of stages");
+  constexpr uint32_t SSTR = WK * TILEB;  // stage stride within the K (or V) region
+  static_assert(NSLOT * SSTR <= kVRegion, "K and V regions of the ring");
+  const uint32_t lring = lds_addr(ring);
+  auto stage_slot = [&](int slot) { return lring + (uint32_t)slot * SSTR; };
+  // The unit's R query rows travel the same way, into ring space that stages 2..
+  // take over only when the prologue ends: rows 0..QRH-1 at offset 32 KB of the K
+  // region, the rest at the same offset of the V region, swizzled like a K tile
+  // (chunk ^ row % CH), so that each wave reads its B operands with the K operand
+  // offsets.  Loaded per lane straight into registers, every instruction would
+  // touch 64 cache lines (32 rows, 16 bytes of each), and both key groups would
+  // fetch the same rows.
+  constexpr int QRH = 32768 / ROWB;       // query rows per 32 KB half
+  constexpr int QRW = R / 8;              // rows loaded per wave
+  constexpr int QPW = QRW * ROWB / 1024;  // loads per wave
+  constexpr int QRPI = 1024 / ROWB;       // rows per load
+  static_assert(2 * SSTR <= 32768 && R <= 2 * QRH && QRH % QRW == 0 && QPW >= 1,
+                "queries fit the ring space of stages 2..");
+  auto q_lds = [&](int r) {
+    return lring + (uint32_t)(r / QRH) * kVRegion + 32768u + (uint32_t)(r % QRH) * ROWB;
+  };
+  {
+    const char* qb = uniform_ptr((const char*)a.q + ((int64_t)u.b * kCanvas * Hq + u.g * G) * ROWB);
+    const int r_first = wave * QRW;
+#pragma unroll
+    for (int j = 0; j < QPW; j += 4) {
+      constexpr int NB4 = QPW < 4 ? QPW : 4;
+      uint32_t vo[NB4];
+#pragma unroll
+      for (int e = 0; e < NB4; e++) {
+        const int r = r_first + (j + e) * QRPI + lane / CH;  // row within the unit
+        const int pr = row0 + r, qq = div_rcp(pr, plan.rcp_g);
+        const int c = (lane % CH) ^ (r % CH);                // logical chunk at this slot
+        vo[e] = (uint32_t)((qq * Hq + pr - qq * G) * ROWB + 16 * c) - 1024u * (uint32_t)e;
+      }
+      gll_block<NB4>(qb, vo, __builtin_amdgcn_readfirstlane(q_lds(r_first + j * QRPI)));
+    }
+  }
+  const int npre = min(2, nstages);
+  for (int st = 0; st < npre; st++) issue_stage<D, WK, 8>(stage_slot(st), kbeg + st * WK * 32, sl);
+
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
-  const int wave_qi_min = (row0 + 32 * rg) / G;
-  const int wave_qi_max = (row0 + 32 * rg + 31) / G;
+  const int wave_qi_min = div_rcp(row0 + 32 * rg, plan.rcp_g);
+  const int wave_qi_max = div_rcp(row0 + 32 * rg + 31, plan.rcp_g);
   const float c2 = a.scale_log2;
   // keys this wave can see: the unit's keys, and for the commit the diagonal
   const int klimit = CAUSAL ? min(kstop, L + wave_qi_max + 1) : kstop;
@@ -529,11 +581,6 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
   }
   const int kmask = tmask > kg ? (tmask - kg + WK - 1) / WK : 0;
 
-  static_assert((NSLOT & (NSLOT - 1)) == 0, "ring of a power-of-two number of stages");
-  constexpr uint32_t SSTR = WK * TILEB;  // stage stride within the K (or V) region
-  static_assert(NSLOT * SSTR <= kVRegion, "K and V regions of the ring");
-  const uint32_t lring = lds_addr(ring);
-  auto stage_slot = [&](int slot) { return lring + (uint32_t)slot * SSTR; };
   auto chunk_key = [&](int k) { return kbeg + (k * WK + kg) * 32; };
   // per-lane operand addresses in stage 0 of this wave's key group
   uint32_t kaddr[KS], vaddr[MB];
@@ -542,19 +589,20 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
 #pragma unroll
   for (int mb = 0; mb < MB; mb++) vaddr[mb] = lring + kVRegion + kg * TILEB + lo.v[mb];
 
-  // ---- prologue: every free stage of the ring is requested; stages 0 and 1
-  //      (the operands of the first chunk and the scores of the second) are waited for
-  // Only stages 0 and 1 are requested before the first wait: the compiler's wait
-  // for the query registers also covers every load issued before it, and the
-  // first chunk needs nothing else.  The rest of the ring follows at once.
-  const int npre = min(2, nstages);
-  for (int st = 0; st < npre; st++) issue_stage<D, WK, 8>(stage_slot(st), kbeg + st * WK * 32, sl);
+  // ---- prologue.  Barrier A: the queries and stage 0 (the wave's own loads of
+  //      them are its oldest npre*GPW .. ones) are in LDS; the wave reads its query
+  //      operands and starts on chunk 0.  Barrier B: stage 1 is in, and every wave
+  //      has read its queries, so the rest of the ring may overwrite them.
+  if (npre == 2)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(GPW) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  bf16x8 qr[KS];    // B operands of S^T = K Q^T: lane (n, h), k-step ks holds
+                    // q[row][D/2*h + 8*ks .. +8] (the permutation of head_dim the K
+                    // operands use too)
 #pragma unroll
-  for (int ks = 0; ks < KS; ks++) asm volatile("" ::"v"(qr[ks]));
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int st = 2; st < min(NSLOT, nstages); st++)
-    issue_stage<D, WK, 8>(stage_slot(st), kbeg + st * WK * 32, sl);
-
+  for (int ks = 0; ks < KS; ks++)
+    qr[ks] = *(const LDS_AS bf16x8*)(uintptr_t)(q_lds(32 * rg) + lo.k[ks]);
   f32x16 s_nx;      // scores of the chunk the next softmax works on
   bf16x8 kop[KS];   // K operands for the next score MFMAs
   bf16x8 vop[MB][2];// V^T operands for the next value MFMAs
@@ -564,13 +612,16 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
     scores<D>(kop, qr, s_nx);
     load_v_operands<D>(vaddr, 0, vop);
   }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  for (int st = 2; st < min(NSLOT, nstages); st++)
+    issue_stage<D, WK, 8>(stage_slot(st), kbeg + st * WK * 32, sl);
   if (1 < nok) load_k_operands<D>(kaddr, SSTR % (NSLOT * SSTR), kop);
   if (0 < nok) {
     prepare_scores<MB, CAUSAL>(s_nx, 0 >= kmask, chunk_key(0), kstop, L, qi, h, c2, acc);
     numerators<MB>(s_nx, c2, acc, pb);
   }
 
-  // Barrier t of the phase sequence (t = 0 is the prologue's): group 0 runs X(k)
+  // Barrier t of the phase sequence (t = 0 is the prologue's B): group 0 runs X(k)
   // after barrier 2k and Y(k) after 2k+1; group 1 runs one barrier later.  Odd
   // barriers 2j+1 carry the ring protocol: before it, stage j+2 must be complete
   // in the wave's share.  Stage j+NSLOT may overwrite stage j once barrier 2j+1
@@ -697,7 +748,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
   for (int k = 0; k < 4; k++) {
     const int p = row0 + 32 * rg + 8 * k + r_lo;  // packed row stored by this lane
     rowp[k] = direct ? (uint16_t*)a.out +
-                           ((int64_t)(u.b * kCanvas + p / G) * Hq + u.g * G + p % G) * D
+                           ((int64_t)(u.b * kCanvas + div_rcp(p, plan.rcp_g)) * Hq + u.g * G + p - div_rcp(p, plan.rcp_g) * G) * D
                      : (uint16_t*)a.part_o + ((int64_t)U * R + (p - row0)) * D;
   }
 #pragma unroll
@@ -796,13 +847,13 @@ void attn_rows_kernel(AttnArgs a, Plan plan) {
   const int wave = uniform(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
   const int U = xcd_remap(blockIdx.x, gridDim.x);
-  const Unit u = decode_unit(plan, U);
-  const SeqPlan sp = plan.seq[u.b];
+  SeqPlan sp;
+  const Unit u = decode_unit(plan, U, sp);
   const int L = sp.prefix_len;
-  const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = Hq / Hkv;
+  const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = plan.g;
   const int row0 = u.rt * R;
   int kend = L + kCanvas;
-  if (CAUSAL) kend = min(kend, L + (row0 + R - 1) / G + 1);
+  if (CAUSAL) kend = min(kend, L + div_rcp(row0 + R - 1, plan.rcp_g) + 1);
   const int kbeg = u.s * sp.split_keys;
   const int kstop = min(kbeg + sp.split_keys, kend);
   const int nstages = kstop > kbeg ? (kstop - kbeg + 31) / 32 : 0;
@@ -836,9 +887,9 @@ void attn_rows_kernel(AttnArgs a, Plan plan) {
 #pragma unroll
   for (int rb = 0; rb < NB; rb++) {
     const int prow = row0 + 32 * NB * wave + 32 * rb + n;
-    qi[rb] = prow / G;
+    qi[rb] = div_rcp(prow, plan.rcp_g);
     const uint16_t* qp = (const uint16_t*)a.q +
-                         ((int64_t)(u.b * kCanvas + qi[rb]) * Hq + u.g * G + prow % G) * D + (D / 2) * h;
+                         ((int64_t)(u.b * kCanvas + qi[rb]) * Hq + u.g * G + prow - qi[rb] * G) * D + (D / 2) * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) qr[rb][ks] = *(const bf16x8*)(qp + 8 * ks);
   }
@@ -850,8 +901,8 @@ void attn_rows_kernel(AttnArgs a, Plan plan) {
                              (const char*)(vn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
                              Hkv * D * 2, L, kstop, wave, lane);
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
-  const int wave_qi_min = (row0 + 32 * NB * wave) / G;
-  const int wave_qi_max = (row0 + 32 * NB * wave + 32 * NB - 1) / G;
+  const int wave_qi_min = div_rcp(row0 + 32 * NB * wave, plan.rcp_g);
+  const int wave_qi_max = div_rcp(row0 + 32 * NB * wave + 32 * NB - 1, plan.rcp_g);
   const float c2 = a.scale_log2;
   // chunks with visible keys for this wave: k < nok; chunks needing masks: k >= kmask
   const int klimit = CAUSAL ? min(kstop, L + wave_qi_max + 1) : kstop;
@@ -967,7 +1018,7 @@ void attn_rows_kernel(AttnArgs a, Plan plan) {
     for (int kk = 0; kk < 4; kk++) {
       const int p = row0 + 32 * NB * wave + 32 * rb + 8 * kk + r_lo;
       rowp[kk] = direct ? (uint16_t*)a.out +
-                              ((int64_t)(u.b * kCanvas + p / G) * Hq + u.g * G + p % G) * D
+                              ((int64_t)(u.b * kCanvas + div_rcp(p, plan.rcp_g)) * Hq + u.g * G + p - div_rcp(p, plan.rcp_g) * G) * D
                         : (uint16_t*)a.part_o + ((int64_t)U * R + (p - row0)) * D;
     }
 #pragma unroll

@@ -25,7 +25,16 @@ struct SeqPlan {
   int32_t n_splits;    // S_b >= 1
   int32_t split_keys;  // keys per split (multiple of 32); the last split may be shorter
   int32_t unit_base;   // first logical unit index of this sequence
+  uint32_t rcp_s;      // div_rcp multipliers of S_b and S_b * NRT
+  uint32_t rcp_snrt;
 };
+
+// Reciprocal multiplier for floor(n / d) when n * d < 2^32: with m = floor(2^32/d) + 1,
+// floor(n*m / 2^32) = floor(n/d), because the excess n*(m - 2^32/d)/2^32 < n/2^32 < 1/d
+// cannot reach the next multiple of d.  d = 1 is encoded as m = 0.  The kernels divide
+// by per-call values (heads per kv head, splits, row tiles) this way: a hardware-free
+// integer division costs tens of dependent instructions before the first load.
+inline uint32_t rcp_u32(uint32_t d) { return d <= 1 ? 0u : (uint32_t)((1ull << 32) / d + 1); }
 
 // bf16 kernel shapes.  R256 and R128: eight waves of 32 packed rows (row groups x
 // key groups, waves paired on a SIMD in ping-pong); F8: eight free-running waves
@@ -37,11 +46,15 @@ inline int variant_rows(int v) { return v == kVariantR128 ? 128 : 256; }
 struct Plan {
   int32_t batch;
   int32_t variant;      // bf16 kernel shape (kVariant*); rows_per_unit follows from it
-  int32_t n_units;      // total logical units = grid size of the attention kernel
+  int32_t n_units;      // total logical units = grid size of the attention kernel (< 2^16)
   int32_t n_rowtiles;   // NRT = 256*G / R
   int32_t rows_per_unit;// R
+  int32_t g;            // G = query heads per kv head
+  uint32_t rcp_g;       // div_rcp multipliers of G and NRT
+  uint32_t rcp_nrt;
   SeqPlan seq[kMaxBatch];
 };
+constexpr int kMaxUnits = 1 << 16;
 
 struct AttnArgs {
   const void* q;        // [B][256][Hq][D]
