@@ -453,7 +453,8 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
   constexpr int SLOTB = WK * 2 * TILEB; // one ring stage: K and V tiles of every key group
   constexpr int GPW = SLOTB / 1024 / 8; // global_load_lds per wave per stage
   static_assert(GPW >= 1 && SLOTB % 8192 == 0, "stage load split");
-  constexpr int PER = MB * 16 + 2;      // floats per lane in the key-group merge
+  constexpr int PER = MB * 16 + 4;      // floats per lane in the key-group merge: O,
+                                        // max, sum, padding to whole 16-byte words
   constexpr int MERGEB = (WK - 1) * WM * 64 * PER * 4;
   static_assert(MERGEB <= NSLOT * SLOTB, "key-group merge fits in the ring");
   __shared__ __attribute__((aligned(1024))) char ring[NSLOT * SLOTB];
@@ -692,30 +693,36 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
         odd_barrier(k + 1, true);
     }
   }
+  // Group 1 passed one more barrier in the loop; this one pairs with it.  From
+  // here on the ring is free: every operand read was waited for at an earlier
+  // barrier (the last ones, of chunk nstages-1 or the unused chunk past a wave's
+  // last, at barrier 2*nstages-1 at the latest) and every stage load at an odd one.
   if (grp == 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // ---- merge the key groups through LDS (group 0 keeps the result).  Every wave
-  //      passes every barrier; only group 0 carries on with the result.
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // ---- merge the key groups through LDS: key groups 1.. leave their state,
+  //      group 0 folds it into its own and writes the rows (one barrier)
   if (WK > 1) {
-    float* mbuf = (float*)ring;
+    // lane-major, PER floats per lane: 16-byte LDS accesses, and the 4-bank step
+    // between lanes keeps each group of 16 lanes on distinct banks
+    float4* mbuf = (float4*)ring;
     if (kg > 0) {
-      float* dst = mbuf + ((kg - 1) * WM + rg) * 64 * PER;
-      int k = 0;
+      float4* dst = mbuf + (((kg - 1) * WM + rg) * 64 + lane) * (PER / 4);
 #pragma unroll
       for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-        for (int i = 0; i < 16; i++) dst[(k++) * 64 + lane] = acc.o[mb][i];
-      dst[(k++) * 64 + lane] = acc.mlog;
-      dst[(k++) * 64 + lane] = acc.lsum;
+        for (int i = 0; i < 4; i++)
+          dst[mb * 4 + i] = make_float4(acc.o[mb][4 * i], acc.o[mb][4 * i + 1],
+                                        acc.o[mb][4 * i + 2], acc.o[mb][4 * i + 3]);
+      dst[MB * 4] = make_float4(acc.mlog, acc.lsum, 0.f, 0.f);
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kg == 0) {
+    if (kg > 0) return;
+    {
 #pragma unroll
       for (int og = 1; og < WK; og++) {
-        const float* srcm = mbuf + ((og - 1) * WM + rg) * 64 * PER;
-        const float m2 = srcm[(MB * 16) * 64 + lane];
-        const float l2 = srcm[(MB * 16 + 1) * 64 + lane];
+        const float4* srcm = mbuf + (((og - 1) * WM + rg) * 64 + lane) * (PER / 4);
+        const float4 ml = srcm[MB * 4];
+        const float m2 = ml.x, l2 = ml.y;
         const float mn = fmaxf(acc.mlog, m2);
         const float a1 = __builtin_amdgcn_exp2f(acc.mlog - mn);
         const float a2 = __builtin_amdgcn_exp2f(m2 - mn);
@@ -724,13 +731,16 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-          for (int i = 0; i < 16; i++)
-            acc.o[mb][i] = acc.o[mb][i] * a1 + srcm[(mb * 16 + i) * 64 + lane] * a2;
+          for (int i = 0; i < 4; i++) {
+            const float4 v = srcm[mb * 4 + i];
+            acc.o[mb][4 * i] = acc.o[mb][4 * i] * a1 + v.x * a2;
+            acc.o[mb][4 * i + 1] = acc.o[mb][4 * i + 1] * a1 + v.y * a2;
+            acc.o[mb][4 * i + 2] = acc.o[mb][4 * i + 2] * a1 + v.z * a2;
+            acc.o[mb][4 * i + 3] = acc.o[mb][4 * i + 3] * a1 + v.w * a2;
+          }
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  if (kg > 0) return;
 
   // ---- write the unit's rows: normalised, rounded to bf16, either as the final
   //      output (single split) or as this split's partial rows.  They go out
@@ -741,7 +751,12 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const bool direct = sp.n_splits == 1;
   constexpr int SROWB = 64 * 2 + 16;  // bytes per staged row (padding spreads banks)
-  char* stage = ring + rg * 32 * SROWB;
+  // staging past the merge buffer, so that no wave's staging overwrites state
+  // another wave is still merging
+  constexpr int STAGE0 = WK > 1 ? kVRegion + 32768 : 0;
+  static_assert(WK == 1 || (MERGEB <= STAGE0 && STAGE0 + WM * 32 * SROWB <= NSLOT * SLOTB),
+                "output staging clear of the merge buffer");
+  char* stage = ring + STAGE0 + rg * 32 * SROWB;
   const int r_lo = lane / 8, cq = lane % 8;  // 8 lanes cover one 128-byte row segment
   uint16_t* rowp[4];
 #pragma unroll
