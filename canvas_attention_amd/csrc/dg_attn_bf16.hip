@@ -426,18 +426,24 @@ __device__ __forceinline__ void values(const bf16x8 (&vop)[MB][2], const bf16x8 
 }
 
 // The kernel.  Wave (rg, kg) processes chunk k = tile k*WK + kg of the unit for
-// k = 0 .. nstages-1; chunk k lives in ring stage k.  Per chunk a wave runs
-//   X(k): O += V(k) P(k) (8 MFMAs), S(k+1) = K(k+1) Q^T (8 MFMAs)
-//   Y(k): V(k+1) and K(k+2) operand reads, softmax of S(k+1) -> P(k+1)
-// Workgroup barriers split time into half-chunk phases; waves 0-3 (group 0) and
-// waves 4-7 (group 1) run the same sequence one phase apart, so that while one
-// wave of a SIMD is in X the other is in Y.
-// Ring protocol: every barrier first waits for the wave's LDS reads, so the
-// last reads of stage j (group 1's V(j), in the phase after barrier 2j) are done
-// at barrier 2j+1, after which stage j+NSLOT may overwrite it; the first reads
-// of stage j+2 (group 0's K(j+2), after barrier 2j+1) need it complete, so
-// before barrier 2j+1 every wave waits for its own loads of stage j+2, with at
-// most the NSLOT-3 later stages left in flight.
+// k = 0 .. nstages-1; chunk k lives in ring stage k (slot k mod NSLOT).  Per chunk
+// a wave runs
+//   X(k): requests stage k+NSLOT, O += V(k) P(k) (8 MFMAs), S(k+1) = K(k+1) Q^T
+//         (8 MFMAs) with the V(k+1) operand reads between them
+//   Y(k): K(k+2) operand reads, softmax of S(k+1) -> P(k+1)
+// One workgroup barrier per chunk: barrier k follows Y(k) in waves 0-3 (group 0)
+// and X(k) in waves 4-7 (group 1), so group 1 runs half a chunk behind and, on
+// each SIMD, one wave is in X while the other is in Y.  Between barriers k-1 and
+// k group 0 runs X(k), Y(k) and group 1 runs Y(k-1), X(k).
+// Ring protocol: every barrier first waits for the wave's LDS reads.  The reads
+// of stage k (V(k) in X(k-1), K(k) in Y(k-2), which for group 1 falls between
+// barriers k-2 and k-1) are then done at barrier k-1, after which X(k) may
+// request stage k+NSLOT into the same slot.  The first read of stage s is group
+// 0's K(s) in Y(s-2), after barrier s-3; so before barrier k every wave waits for
+// its own loads of stage k+3, leaving stages k+4 .. k+NSLOT in flight.  Stage 2
+// is requested only after the prologue (its slot holds the queries until then),
+// yet group 0 reads K(2) in Y(0); one extra barrier E, after group 0's X(0) and
+// before group 1's X(0), waits for it.
 template <int D, bool CAUSAL, int WM, int WK, int NSLOT>
 __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan) {
   static_assert(WM * WK == 8, "eight waves: row groups x key groups");
@@ -622,31 +628,23 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
     numerators<MB>(s_nx, c2, acc, pb);
   }
 
-  // Barrier t of the phase sequence (t = 0 is the prologue's B): group 0 runs X(k)
-  // after barrier 2k and Y(k) after 2k+1; group 1 runs one barrier later.  Odd
-  // barriers 2j+1 carry the ring protocol: before it, stage j+2 must be complete
-  // in the wave's share.  Stage j+NSLOT may overwrite stage j once barrier 2j+1
-  // has passed; each wave requests it at the start of its next MFMA phase
-  // (group 0: X(j+1), group 1: X(j)), where the issue slots are free.
-  // LDS reads: a wave reads V(j) in X(j-1) and K(j) in Y(j-2).  The barrier that
-  // ends each Y waits for the wave's outstanding LDS reads, so by barrier 2j+1
-  // every read of stage j is complete (group 1's V(j), issued before barrier 2j,
-  // is covered by its Y(j-1) barrier, which is 2j+1 itself).
-  auto odd_barrier = [&](int j, bool lgkm) {
-    if (j + NSLOT <= nstages) {
-      if (lgkm)
+  auto barrier_e = [&](bool after_x0) {  // barrier E: stage 2 complete
+    if (NSLOT < nstages) {
+      if (after_x0)  // stages 3 .. NSLOT may be in flight
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NSLOT - 2) * GPW) : "memory");
+      else           // stages 3 .. NSLOT-1 may be in flight
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NSLOT - 3) * GPW) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSLOT - 3) * GPW) : "memory");
     } else {
-      if (lgkm)
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
   };
+  auto ring_barrier = [&](int k) {  // barrier k (see the kernel comment)
+    if (k + NSLOT < nstages)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NSLOT - 3) * GPW) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
 
-  if (grp == 1) odd_barrier(0, true);
   // The chunk loop is unrolled over the ring so that every stage offset is a
   // compile-time immediate of the LDS instructions.
   for (int k0 = 0; k0 < nstages; k0 += NSLOT) {
@@ -655,15 +653,12 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
       const int k = k0 + j;
       if (k >= nstages) break;
       const uint32_t off1 = ((j + 1) % NSLOT) * SSTR, off2 = ((j + 2) % NSLOT) * SSTR;
-      // X(k): loads of stage k+NSLOT-1+grp; the value product of chunk k; the V
-      // operands of chunk k+1 read while the scores of chunk k+1 run (the issue
-      // slots of an MFMA phase are otherwise idle)
+      // X(k): loads of stage k+NSLOT (into the slot of stage k); the value
+      // product of chunk k; the V operands of chunk k+1 read while the scores of
+      // chunk k+1 run (the issue slots of an MFMA phase are otherwise idle)
       __builtin_amdgcn_sched_barrier(0);
-      {
-        const int st = k + NSLOT - 1 + grp;
-        if (st >= NSLOT && st < nstages)
-          issue_stage<D, WK, 8>(stage_slot((j + NSLOT - 1 + grp) & (NSLOT - 1)), kbeg + st * WK * 32, sl);
-      }
+      if (grp == 1 && k == 0) barrier_e(false);
+      if (k + NSLOT < nstages) issue_stage<D, WK, 8>(stage_slot(j), kbeg + (k + NSLOT) * WK * 32, sl);
       __builtin_amdgcn_s_setprio(1);
       if (k < nok) values<MB>(vop, pb, acc);
       if (k + 1 < nok) {
@@ -677,7 +672,8 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
       }
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      if (grp == 0) odd_barrier(k, false); else asm volatile("s_barrier" ::: "memory");
+      if (grp == 1) ring_barrier(k);
+      else if (k == 0) barrier_e(true);
       __builtin_amdgcn_sched_barrier(0);
       // Y(k): K operands of chunk k+2 (for X(k+1); a chunk past the wave's last is
       // read too and not used), softmax of chunk k+1 (vector ALU)
@@ -687,17 +683,12 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
         numerators<MB>(s_nx, c2, acc, pb);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (grp == 0)
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      else
-        odd_barrier(k + 1, true);
+      if (grp == 0) ring_barrier(k);
     }
   }
-  // Group 1 passed one more barrier in the loop; this one pairs with it.  From
-  // here on the ring is free: every operand read was waited for at an earlier
-  // barrier (the last ones, of chunk nstages-1 or the unused chunk past a wave's
-  // last, at barrier 2*nstages-1 at the latest) and every stage load at an odd one.
-  if (grp == 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // From here on the ring is free: every operand read and every stage load was
+  // waited for at barrier nstages-1 at the latest (group 1's last Y, after it,
+  // reads nothing).
 
   // ---- merge the key groups through LDS: key groups 1.. leave their state,
   //      group 0 folds it into its own and writes the rows (one barrier)
