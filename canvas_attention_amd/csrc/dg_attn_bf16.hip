@@ -127,7 +127,30 @@ struct State {
   f32x16 o[MB];  // O^T accumulators: lane (n, h) holds d = 32mb + 8(i/4) + 4h + i%4 of query n
   float mlog;    // reference max of the lane's query, log2 domain
   float lsum;    // sum of this lane's exponentials (the partner lane holds the rest)
+  float thr;     // raw score above which a chunk raises the reference:
+                 // (mlog + threshold) / c2, kept with mlog
 };
+
+// Max of the 16 scores of a lane as one chain of v_max3 (written as a single asm
+// block: separate ones each get a wait state).  fmaxf would add canonicalizing
+// instructions (IEEE NaN quieting) that nothing here needs: scores are finite or
+// -inf.  Dependent vector ALU instructions need no wait states between them.
+__device__ __forceinline__ float max16(const f32x16& s) {
+  float m;
+  asm("v_max3_f32 %0, %1, %2, %3\n\t"
+      "v_max3_f32 %0, %0, %4, %5\n\t"
+      "v_max3_f32 %0, %0, %6, %7\n\t"
+      "v_max3_f32 %0, %0, %8, %9\n\t"
+      "v_max3_f32 %0, %0, %10, %11\n\t"
+      "v_max3_f32 %0, %0, %12, %13\n\t"
+      "v_max3_f32 %0, %0, %14, %15\n\t"
+      "v_max_f32 %0, %0, %16"
+      : "=&v"(m)
+      : "v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3]), "v"(s[4]), "v"(s[5]), "v"(s[6]),
+        "v"(s[7]), "v"(s[8]), "v"(s[9]), "v"(s[10]), "v"(s[11]), "v"(s[12]), "v"(s[13]),
+        "v"(s[14]), "v"(s[15]));
+  return m;
+}
 
 // global_load_lds_dwordx4: every lane copies 16 bytes from its global address
 // into LDS at m0 + instruction offset + 16*lane.  Issued from inline asm so that
@@ -367,14 +390,14 @@ __device__ __forceinline__ void prepare_scores(f32x16& s, bool masked, int key0,
       s[i] = ok ? s[i] : -INFINITY;
     }
   }
-  float m = s[0];
-#pragma unroll
-  for (int i = 1; i < 16; i++) m = fmaxf(m, s[i]);
-  const float cm = m * c2;
-  if (__any(cm > acc.mlog + kRescaleThreshold)) {
-    const float mnew = fmaxf(acc.mlog, partner_max(cm));
+  const float m = max16(s);
+  // m > thr stands for m*c2 > mlog + threshold (c2 > 0); a rounding difference
+  // at the boundary moves the exponent bound by far less than its headroom
+  if (__any(m > acc.thr)) {
+    const float mnew = fmaxf(acc.mlog, partner_max(m * c2));
     const float alpha = __builtin_amdgcn_exp2f(acc.mlog - mnew);
     acc.mlog = mnew;
+    acc.thr = (mnew + kRescaleThreshold) / c2;
     acc.lsum *= alpha;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++)
@@ -574,6 +597,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
     for (int i = 0; i < 16; i++) acc.o[mb][i] = 0.f;
   acc.mlog = -1e30f;  // log2-domain reference max; finite so rescales never form inf-inf
   acc.lsum = 0.f;
+  acc.thr = (acc.mlog + kRescaleThreshold) / c2;
 
   // Chunk k of this wave is tile t = k*WK + kg of the unit (keys kbeg + 32t ..).
   // It holds visible keys iff k < nok; its scores need masking iff k >= kmask
@@ -673,7 +697,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       if (grp == 1) ring_barrier(k);
-      else if (k == 0) barrier_e(true);
+      if (grp == 0 && k == 0) barrier_e(true);
       __builtin_amdgcn_sched_barrier(0);
       // Y(k): K operands of chunk k+2 (for X(k+1); a chunk past the wave's last is
       // read too and not used), softmax of chunk k+1 (vector ALU)
