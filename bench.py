@@ -140,6 +140,50 @@ def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib):
     print("\n".join(lines))
 
 
+def summarize_mfma(pass1_dir, pass2_dir, trace_txt):
+    """MFMA work of the canvas attention kernel from two rocprofv3 --pmc runs of
+    `bench.py --steps 2 --warmup 1 --profile-steps` (SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_INSTS_MFMA; SQ_INSTS_VALU_MFMA_MOPS_BF16), set against the kernel's average
+    duration from the kernel-trace summary.  Writes profiles/canvas_attn_l8k_mfma.txt."""
+    import csv
+    import collections
+
+    def per_dispatch(d):
+        vals = collections.defaultdict(lambda: collections.defaultdict(float))
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if ATTN_KERNEL in r["Kernel_Name"]:
+                vals[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {c: (sum(v.values()) / len(v), len(v)) for c, v in vals.items()}
+
+    c = {**per_dispatch(pass1_dir), **per_dispatch(pass2_dir)}
+    avg_us = None
+    for line in open(trace_txt):
+        if ATTN_KERNEL in line:
+            avg_us = float(line.split()[1])
+    busy = c["SQ_VALU_MFMA_BUSY_CYCLES"][0] / 1024.0  # per SIMD (256 CUs x 4)
+    mops = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"][0]
+    out = os.path.join(ROOT, "profiles", "canvas_attn_l8k_mfma.txt")
+    with open(out, "w") as f:
+        f.write("# MFMA work of the canvas attention kernel (canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)\n")
+        f.write("# from rocprofv3 --pmc runs (each in its own process) of\n")
+        f.write("#   python3 bench.py --steps 2 --warmup 1 --profile-steps\n")
+        f.write("#   pass 1: SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_MFMA\n")
+        f.write("#   pass 2: SQ_INSTS_VALU_MFMA_MOPS_BF16\n")
+        f.write("# per-dispatch means over the dispatches of the kernel; written by\n")
+        f.write("#   python3 bench.py --summarize-mfma PASS1 PASS2 profiles/canvas_attn_l8k_kernel_trace.txt\n")
+        f.write(f"kernel: {ATTN_KERNEL}...>\n")
+        f.write(f"kernel_source_hash: {kernel_source_hash()}\n")
+        f.write(f"dispatches: {c['SQ_INSTS_MFMA'][1]}\n")
+        f.write(f"mfma_instructions: {c['SQ_INSTS_MFMA'][0]:.0f}\n")
+        f.write(f"mfma_flop (MOPS_BF16 x 512): {mops * 512:.4e}\n")
+        f.write(f"algorithmic_flop: {step_flops(1, 16, 8192, 128):.4e}\n")
+        f.write(f"mfma_busy_cycles_per_simd: {busy:.0f}\n")
+        if avg_us:
+            f.write(f"kernel_avg_us (kernel trace): {avg_us}\n")
+            f.write(f"mfma_busy_frac_at_2.4GHz: {busy / (avg_us * 1e-6 * 2.4e9):.4f}\n")
+    print(open(out).read())
+
+
 def summarize_trace(stats_csv, out_txt):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
@@ -185,6 +229,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH", "WRITE", "COPY_FETCH",
                                                               "COPY_WRITE", "COPY_MIB"),
                     help="write the traffic file from four rocprofv3 --pmc output folders")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("PASS1", "PASS2", "TRACE_TXT"),
+                    help="write profiles/canvas_attn_l8k_mfma.txt from two rocprofv3 --pmc runs")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "OUT_TXT"),
                     help="write a kernel summary from a rocprofv3 --stats kernel_stats.csv")
     args = ap.parse_args()
@@ -193,6 +239,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the canvas "
@@ -279,6 +328,32 @@ def main():
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / (args.steps * n_steps)
 
+    # per-launch kernel durations (the library's events around each launch), median
+    # over calls of one canvas step (attention + merge): warm (the fixed cache stays
+    # in the 256 MB last-level cache, as in a block's step loop) and cold (a 512 MB
+    # scratch fill before every call, outside the timed kernels)
+    reps = max(args.steps, 50)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def one_step(i):
+        s = i % n_steps
+        dg.canvas_attn(qs[s], kc_d, vc_d, L, ks[s], vs[s], out=out_steps[s], workspace=ws)
+
+    medians = {}
+    for mode in ("warm", "cold"):
+        dg.kernel_timing_read()
+        dg.kernel_timing_enable(True)
+        for i in range(reps):
+            if mode == "cold":
+                flush.fill_(i & 255)
+            one_step(i)
+        a_ms, m_ms = dg.kernel_timing_samples(reps)
+        dg.kernel_timing_enable(False)
+        m_ms = m_ms if len(m_ms) == len(a_ms) else [0.0] * len(a_ms)
+        medians[mode] = {"attn": round(float(np.median(a_ms)) * 1e3, 3),
+                         "step": round(float(np.median(np.add(a_ms, m_ms))) * 1e3, 3)}
+    del flush
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -299,6 +374,8 @@ def main():
         "canvas_step_tflops": round(fl_step / (step_ms * 1e-3) / 1e12, 2),
         "canvas_positions_per_s": round(B * 256 / (step_ms * 1e-3), 1),
         "canvas_step_mfma_frac": round(fl_step / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "canvas_call_us_median": {"warm": medians["warm"], "cold": medians["cold"],
+                                  "calls": reps},
         "kernels_us": {"canvas_attn": round(attn_us, 3), "canvas_merge": round(merge_us, 3),
                        "commit_attn": round(cattn_ms / max(n_cattn, 1) * 1e3, 3),
                        "commit_merge": round(cmerge_ms / max(n_cmerge, 1) * 1e3, 3)

@@ -375,6 +375,26 @@ dg_status dg_kernel_timing_enable(int32_t enable) {
   return DG_OK;
 }
 
+dg_status dg_kernel_timing_samples(float* attn_ms, float* merge_ms, int32_t max_n,
+                                   int32_t* n_attn, int32_t* n_merge) {
+  float* dst[2] = {attn_ms, merge_ms};
+  for (int kind = 0; kind < 2; kind++) {
+    for (int k = 0; k < g_timing.count[kind]; k++) {
+      if (hipEventSynchronize(g_timing.ev[kind][k][1]) != hipSuccess)
+        return fail(DG_ERR_HIP, "hipEventSynchronize failed");
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, g_timing.ev[kind][k][0], g_timing.ev[kind][k][1]) !=
+          hipSuccess)
+        return fail(DG_ERR_HIP, "hipEventElapsedTime failed");
+      if (dst[kind] && k < max_n) dst[kind][k] = ms;
+    }
+  }
+  if (n_attn) *n_attn = g_timing.count[0];
+  if (n_merge) *n_merge = g_timing.count[1];
+  g_timing.count[0] = g_timing.count[1] = 0;
+  return DG_OK;
+}
+
 dg_status dg_kernel_timing_read(int32_t* n_attn, double* attn_ms, int32_t* n_merge,
                                 double* merge_ms) {
   double tot[2] = {0, 0};

@@ -70,10 +70,13 @@ lib.dg_kernel_timing_enable.restype = _i32
 lib.dg_kernel_timing_read.argtypes = [_P(_i32), _P(ctypes.c_double), _P(_i32),
                                       _P(ctypes.c_double)]
 lib.dg_kernel_timing_read.restype = _i32
+lib.dg_kernel_timing_samples.argtypes = [_P(ctypes.c_float), _P(ctypes.c_float), _i32, _P(_i32),
+                                         _P(_i32)]
+lib.dg_kernel_timing_samples.restype = _i32
 
 EXPORTS = ["dg_workspace_bytes", "dg_canvas_attn", "dg_commit_block", "dg_canvas_step_loop",
            "dg_status_string", "dg_last_error", "dg_kernel_timing_enable",
-           "dg_kernel_timing_read"]
+           "dg_kernel_timing_read", "dg_kernel_timing_samples"]
 
 
 def _check(fn, status):
@@ -221,6 +224,16 @@ def canvas_step_loop(q_steps, k_steps, v_steps, k_cache, v_cache, prefix_len, ou
 
 def kernel_timing_enable(on: bool = True):
     _check("dg_kernel_timing_enable", lib.dg_kernel_timing_enable(1 if on else 0))
+
+
+def kernel_timing_samples(max_n: int = 4096):
+    """(attn_ms list, merge_ms list): per-launch durations since the previous read."""
+    a = (ctypes.c_float * max_n)()
+    m = (ctypes.c_float * max_n)()
+    na, nm = ctypes.c_int32(), ctypes.c_int32()
+    _check("dg_kernel_timing_samples",
+           lib.dg_kernel_timing_samples(a, m, max_n, ctypes.byref(na), ctypes.byref(nm)))
+    return list(a[:min(na.value, max_n)]), list(m[:min(nm.value, max_n)])
 
 
 def kernel_timing_read():

@@ -166,6 +166,15 @@ const char* dg_last_error(void);
 dg_status dg_kernel_timing_enable(int32_t enable);
 dg_status dg_kernel_timing_read(int32_t* n_attn, double* attn_ms, int32_t* n_merge,
                                 double* merge_ms);
+/*
+ * Like dg_kernel_timing_read, but returns the duration of every recorded launch
+ * (milliseconds, in launch order) instead of sums: up to max_n attention kernels
+ * into attn_ms and up to max_n merge kernels into merge_ms (host arrays owned by
+ * the caller; either may be NULL to skip that kind).  *n_attn and *n_merge get
+ * the numbers recorded, which may exceed max_n.  Clears the record.
+ */
+dg_status dg_kernel_timing_samples(float* attn_ms, float* merge_ms, int32_t max_n,
+                                   int32_t* n_attn, int32_t* n_merge);
 
 #ifdef __cplusplus
 }
