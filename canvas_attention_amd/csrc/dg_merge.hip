@@ -26,25 +26,33 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return x * (n / kNumXcd) + min(x, n % kNumXcd) + j;
 }
 
+// floor(n / d) from the host's reciprocal multiplier m = rcp_u32(d), valid for
+// n*d < 2^32 (m = 0 encodes d = 1)
+__device__ __forceinline__ int div_rcp(int n, uint32_t m) {
+  return (int)__umulhi((uint32_t)n, m) + (m == 0u ? n : 0);
+}
+
 // Partial rows are bf16 for the bf16 path and fp32 for the fp32 path; each thread
-// combines 8 (bf16) or 4 (fp32) adjacent head_dim elements of one row.
+// combines 8 (bf16) or 4 (fp32) adjacent head_dim elements of one row.  Block
+// (x, y) covers rows x*RPB .. of sequence y.  Index math avoids runtime integer
+// division (tens of dependent instructions each, ahead of the first load): G
+// through the plan's reciprocal, the rows per unit (a power of two) by a shift.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
   constexpr int EPT = BF16 ? 8 : 4;  // elements per thread
   constexpr int TPR = D / EPT;       // threads per row
   constexpr int RPB = 256 / TPR;     // rows per block
-  const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = Hq / Hkv;
-  const int rows_per_seq = Hkv * kCanvas * G;
-  const int64_t grow = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * RPB + threadIdx.x / TPR;
-  const int dq = threadIdx.x % TPR;
-  if (grow >= (int64_t)plan.batch * rows_per_seq) return;
-  const int b = (int)(grow / rows_per_seq);
-  const int rem = (int)(grow % rows_per_seq);
-  const int g = rem / (kCanvas * G), p = rem % (kCanvas * G);
+  const int Hq = a.n_heads_q, G = plan.g;
+  const int b = blockIdx.y;
   const SeqPlan sp = plan.seq[b];
   if (sp.n_splits == 1) return;  // written directly by the attention kernel
-  const int R = plan.rows_per_unit, NRT = plan.n_rowtiles;
-  const int rt = p / R, pr = p % R;
+  const int rem = xcd_remap(blockIdx.x, gridDim.x) * RPB + threadIdx.x / TPR;  // row of sequence b
+  const int dq = threadIdx.x % TPR;
+  if (rem >= Hq * kCanvas) return;
+  const int g = div_rcp(rem / kCanvas, plan.rcp_g), p = rem - g * (kCanvas * G);
+  const int rsh = __builtin_ctz((unsigned)plan.rows_per_unit), NRT = plan.n_rowtiles;
+  const int rt = p >> rsh, pr = p & (plan.rows_per_unit - 1);
+  const int R = plan.rows_per_unit;
   const int u0 = sp.unit_base + g * sp.n_splits * NRT + rt;
 
   // Splits are visited in batches of 8 with all loads of a batch in flight at
@@ -91,7 +99,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
     M = Mb;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const int i = p / G, hh = p % G;
+  const int i = div_rcp(p, plan.rcp_g), hh = p - i * G;
   const int64_t off = ((int64_t)(b * kCanvas + i) * Hq + g * G + hh) * D + EPT * dq;
   if (BF16) {
     typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -108,9 +116,9 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
 template <int D, bool BF16OUT>
 int launch_t(const AttnArgs& a, const Plan& p, hipStream_t st) {
   constexpr int RPB = 256 / (D / (BF16OUT ? 8 : 4));
-  const int64_t rows = (int64_t)p.batch * a.n_heads_q * kCanvas;
-  const int blocks = (int)((rows + RPB - 1) / RPB);
-  hipLaunchKernelGGL((merge_kernel<D, BF16OUT>), dim3(blocks), dim3(256), 0, st, a, p);
+  const int rows = a.n_heads_q * kCanvas;  // per sequence
+  hipLaunchKernelGGL((merge_kernel<D, BF16OUT>), dim3((rows + RPB - 1) / RPB, p.batch), dim3(256), 0,
+                     st, a, p);
   return (int)hipGetLastError();
 }
 
