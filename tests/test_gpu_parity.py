@@ -120,6 +120,36 @@ def test_canvas_small_shapes(oracle_lib, split_keys, B, L, Hq, Hkv, D, forced):
     print(f"B={B} L={L} G={Hq // Hkv} D={D} split={forced}: err {err:.2e}")
 
 
+@pytest.mark.parametrize("forced", [128, 160, 192, 256, 288, 352, 416])
+@pytest.mark.parametrize("L", [100, 190])
+def test_canvas_ring_depths(oracle_lib, split_keys, forced, L):
+    """Units of 2 .. 7 ring stages (64 keys each in the default shape), with the
+    cache/canvas seam inside different stages: the first-chunk barrier and the tail
+    of the ring protocol take their counted and their full waits."""
+    split_keys(forced)
+    c = make(31, 1, [L], 16, 8, 128, "bf16")
+    err = check_canvas(c, TOL_BF16)
+    print(f"L={L} split={forced}: err {err:.2e}")
+
+
+@pytest.mark.parametrize("forced", [128, 192, 288, 416])
+def test_commit_ring_depths(oracle_lib, split_keys, forced):
+    """The causal commit over units of 2 .. 7 stages, with the seam and the
+    diagonal in the same units."""
+    split_keys(forced)
+    Ls = np.asarray([150], np.int32)
+    cap = int(Ls.max()) + 256
+    kc, vc = synth.cache(32, Ls, cap, 8, 128, "bf16")
+    qb, kb, vb = synth.block(32, 1, 16, 8, 128, "bf16")
+    kc_d, vc_d = to_dev(kc), to_dev(vc)
+    out = dg.commit_block(to_dev(qb), to_dev(kb), to_dev(vb), kc_d, vc_d, Ls)
+    torch.cuda.synchronize()
+    ref = oracle_lib.commit_attn(qb, kc, vc, Ls, kb, vb)
+    err = row_err(to_host_f64(out), ref)
+    assert err <= TOL_BF16, err
+    print(f"commit split={forced}: err {err:.2e}")
+
+
 def test_canvas_long_context_sampled(oracle_lib):
     """bf16 L=131072: split-key merge and cache streaming; sampled rows."""
     w = synth.WORKLOADS["long_l128k"]
