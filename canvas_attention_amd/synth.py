@@ -9,7 +9,8 @@ Recipe (the same for every workload):
     with one seed per workload and tensor ids 0/1 cache K/V, 2/3/4 canvas Q/K/V,
     5/6/7 commit (block) Q/K/V;
   * values: ``standard_normal`` drawn in float32, stored as bf16 by rounding to
-    nearest-even (fp32 workloads keep the float32 values);
+    nearest-even (fp32 workloads keep the float32 values; fp8 workloads store
+    OCP e4m3 bytes, rounded to nearest-even, with tensor scales of 1);
   * layout: row-major [B, rows, heads, head_dim]; each sequence is drawn with its
     own ``seq`` index, so a sequence's data does not depend on the batch size.
 
@@ -67,6 +68,27 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return r
 
 
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP e4m3 bytes (uint8): round to nearest, ties to even; finite
+    magnitudes beyond the largest value 448 (and infinities) saturate to it, NaN
+    becomes 0x7f.
+
+    Within binade [2^e, 2^(e+1)), e >= -6, the representable magnitudes are
+    q * 2^(e-3) with q = 8..16, and their byte is 8 * (e + 6) + q (below 2^-6 the
+    subnormals m * 2^-9 follow the same rule with e = -6, q = m), so rounding
+    a / 2^(e-3) to the nearest even integer rounds the byte the same way."""
+    x = np.ascontiguousarray(x, dtype=np.float32).astype(np.float64)
+    nan = np.isnan(x)
+    a = np.minimum(np.abs(np.where(nan, 0.0, x)), 448.0)
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))  # a = f * 2^ex, f in [0.5, 1)
+    e = np.minimum(ex - 1, 8)
+    q = np.rint(a / np.exp2(e - 3))             # exact division; rint ties to even
+    code = (8 * (e + 6) + q).astype(np.uint8)
+    code |= np.signbit(x).astype(np.uint8) << 7
+    code[nan] = 0x7F
+    return code
+
+
 def bf16_to_f32(u: np.ndarray) -> np.ndarray:
     """bf16 bit patterns (uint16) -> float32, exact."""
     return (np.ascontiguousarray(u, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
@@ -78,14 +100,19 @@ def bf16_to_f64(u: np.ndarray) -> np.ndarray:
 
 def draw(seed: int, tensor_id: int, shape, dtype: str, seq: int = 0, block: int = 0,
          step: int = 0) -> np.ndarray:
-    """One tensor of N(0,1) values: uint16 bf16 bits for "bf16", float32 for "f32"."""
+    """One tensor of N(0,1) values: uint16 bf16 bits for "bf16", uint8 e4m3 bits
+    for "fp8", float32 for "f32"."""
     rng = np.random.default_rng([seed, tensor_id, seq, block, step])
     x = rng.standard_normal(size=tuple(shape), dtype=np.float32)
-    return bf16_round(x) if dtype == "bf16" else x
+    if dtype == "bf16":
+        return bf16_round(x)
+    if dtype == "fp8":
+        return e4m3_round(x)
+    return x
 
 
 def _storage(dtype: str):
-    return np.uint16 if dtype == "bf16" else np.float32
+    return {"bf16": np.uint16, "fp8": np.uint8}.get(dtype, np.float32)
 
 
 def batched(seed: int, tensor_id: int, batch: int, rows: int, heads: int, d: int, dtype: str,

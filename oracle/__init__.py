@@ -24,8 +24,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dg_oracle.c")
 _LIB = os.path.join(_HERE, "libdg_oracle.so")
 
-BF16, F32, F64 = 0, 1, 2
-_DTYPE_OF = {np.dtype(np.uint16): BF16, np.dtype(np.float32): F32, np.dtype(np.float64): F64}
+BF16, F32, F64, FP8 = 0, 1, 2, 3
+# bf16 and e4m3 travel as their bit patterns (uint16, uint8)
+_DTYPE_OF = {np.dtype(np.uint16): BF16, np.dtype(np.float32): F32, np.dtype(np.float64): F64,
+             np.dtype(np.uint8): FP8}
 
 _lib = None
 
@@ -47,7 +49,8 @@ def _load():
             build(force=False)
         lib = ctypes.CDLL(_LIB)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        attn_args = [i32, i32, i32, i32, i32, i32, dbl, vp, vp, vp, i64, vp, vp, vp, i32, vp, vp]
+        attn_args = [i32, i32, i32, i32, i32, i32, dbl, vp, vp, vp, i64, vp, vp, vp, i32, vp, vp,
+                     dbl, dbl, dbl]
         for name in ("dgo_canvas_attn", "dgo_commit_attn"):
             fn = getattr(lib, name)
             fn.argtypes = attn_args
@@ -74,11 +77,12 @@ def _dtype(*arrays) -> int:
         raise TypeError(f"mixed element types: {dts}")
     dt = dts.pop()
     if dt not in _DTYPE_OF:
-        raise TypeError(f"unsupported element type {dt} (bf16 bits as uint16, float32, float64)")
+        raise TypeError(f"unsupported element type {dt} (bf16 bits as uint16, e4m3 bits as "
+                        "uint8, float32, float64)")
     return _DTYPE_OF[dt]
 
 
-def _attn(fn_name, q, k_cache, v_cache, prefix_len, k_new, v_new, scale, rows):
+def _attn(fn_name, q, k_cache, v_cache, prefix_len, k_new, v_new, scale, rows, tensor_scales):
     lib = _load()
     arrays = [np.ascontiguousarray(x) for x in (q, k_cache, v_cache, k_new, v_new)]
     q, k_cache, v_cache, k_new, v_new = arrays
@@ -95,9 +99,11 @@ def _attn(fn_name, q, k_cache, v_cache, prefix_len, k_new, v_new, scale, rows):
         rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
         n_rows = rows_arr.shape[0]
         out = np.empty((n_rows, D), np.float64)
+    qs, ks, vs = (1.0, 1.0, 1.0) if tensor_scales is None else (float(x) for x in tensor_scales)
     rc = getattr(lib, fn_name)(dt, B, Nc, Hq, Hkv, D, float(scale), _ptr(q), _ptr(k_cache),
                                _ptr(v_cache), cap, _ptr(pl), _ptr(k_new), _ptr(v_new), n_rows,
-                               _ptr(rows_arr) if rows_arr is not None else None, _ptr(out))
+                               _ptr(rows_arr) if rows_arr is not None else None, _ptr(out),
+                               qs, ks, vs)
     if rc != 0:
         raise ValueError(f"{fn_name} rejected its arguments (code {rc})")
     return out
@@ -108,19 +114,22 @@ def num_threads() -> int:
     return int(_load().dgo_num_threads())
 
 
-def canvas_attn(q, k_cache, v_cache, prefix_len, k_canvas, v_canvas, scale=None, rows=None):
+def canvas_attn(q, k_cache, v_cache, prefix_len, k_canvas, v_canvas, scale=None, rows=None,
+                tensor_scales=None):
     """Canvas step: every canvas row attends, unmasked, to cache rows 0..L-1 and
     canvas rows 0..Nc-1.  Returns fp64 [B,Nc,Hq,D], or [len(rows),D] for a list
-    of (b, i, h) rows."""
+    of (b, i, h) rows.  tensor_scales = (q, k, v) multiplies the stored values
+    (for e4m3 inputs; default 1)."""
     return _attn("dgo_canvas_attn", q, k_cache, v_cache, prefix_len, k_canvas, v_canvas,
-                 scale, rows)
+                 scale, rows, tensor_scales)
 
 
-def commit_attn(q_blk, k_cache, v_cache, prefix_len, k_blk, v_blk, scale=None, rows=None):
+def commit_attn(q_blk, k_cache, v_cache, prefix_len, k_blk, v_blk, scale=None, rows=None,
+                tensor_scales=None):
     """Commit attention: block row i attends to cache rows 0..L-1 and block rows
     0..i (causal).  Same output convention as canvas_attn."""
     return _attn("dgo_commit_attn", q_blk, k_cache, v_cache, prefix_len, k_blk, v_blk,
-                 scale, rows)
+                 scale, rows, tensor_scales)
 
 
 def append_block(k_blk, v_blk, k_cache, v_cache, prefix_len):

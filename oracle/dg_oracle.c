@@ -23,9 +23,10 @@
  *    appended to the cache at rows L..L+Nc-1.  The earlier context is not
  *    re-encoded: cache rows 0..L-1 are left as they are.
  *
- * Precision: every input element is widened exactly to double (bf16 and fp32
- * are subsets of fp64); scores, exponentials, sums and the weighted sum are
- * all fp64 with libm exp().  Two passes per row: all scores first, then the
+ * Precision: every input element is widened exactly to double (bf16, fp32 and
+ * e4m3 are subsets of fp64); an e4m3 element is then multiplied by its tensor's
+ * scale (the value it stands for).  Scores, exponentials, sums and the weighted
+ * sum are all fp64 with libm exp().  Two passes per row: all scores first, then the
  * max-shifted exponentials.  No blocking, no online softmax, no reordering
  * beyond the definition.
  *
@@ -38,10 +39,25 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { DGO_BF16 = 0, DGO_F32 = 1, DGO_F64 = 2 };
+enum { DGO_BF16 = 0, DGO_F32 = 1, DGO_F64 = 2, DGO_FP8 = 3 };
+
+/*
+ * OCP 8-bit floating point, E4M3 variant ("OCP 8-bit Floating Point
+ * Specification", E4M3 encoding): 1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits.  Exponent field 0 holds the subnormals m/8 * 2^-6; the all-ones
+ * exponent field is an ordinary binade except mantissa 111, which is NaN (so the
+ * largest finite magnitude is 1.75 * 2^8 = 448 and there are no infinities).
+ */
+static double e4m3_value(uint8_t c) {
+  const int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
 
 /* Exact widening of one stored element to double. */
 static double ld(const void* p, int dtype, int64_t i) {
+  if (dtype == DGO_FP8) return e4m3_value(((const uint8_t*)p)[i]);
   if (dtype == DGO_BF16) {
     uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
     float f;
@@ -53,7 +69,7 @@ static double ld(const void* p, int dtype, int64_t i) {
 }
 
 static size_t elem_size(int dtype) {
-  return dtype == DGO_BF16 ? 2 : (dtype == DGO_F32 ? 4 : 8);
+  return dtype == DGO_FP8 ? 1 : dtype == DGO_BF16 ? 2 : (dtype == DGO_F32 ? 4 : 8);
 }
 
 typedef struct {
@@ -64,6 +80,9 @@ typedef struct {
   const int32_t* prefix_len;
   const void *k_new, *v_new; /* canvas (step) or block (commit) K/V */
   int causal;                /* 0: canvas step, 1: commit */
+  double qs, ks, vs;         /* per-tensor scales of q, K (cache and new) and V: the
+                                value of an element is scale * stored value (1 for
+                                bf16 / fp32 / fp64 inputs) */
 } dgo_args;
 
 /*
@@ -90,7 +109,8 @@ static void attend_row(const dgo_args* a, int b, int i, int h, double* scores, d
       k_off = (((int64_t)b * a->Nc + (j - L)) * a->Hkv + g) * D;
     }
     double s = 0.0;
-    for (int d = 0; d < D; d++) s += ld(a->q, a->dtype, q_off + d) * ld(kp, a->dtype, k_off + d);
+    for (int d = 0; d < D; d++)
+      s += (a->qs * ld(a->q, a->dtype, q_off + d)) * (a->ks * ld(kp, a->dtype, k_off + d));
     s *= a->scale;
     scores[j] = s;
     if (s > m) m = s;
@@ -110,7 +130,7 @@ static void attend_row(const dgo_args* a, int b, int i, int h, double* scores, d
       vp = a->v_new;
       v_off = (((int64_t)b * a->Nc + (j - L)) * a->Hkv + g) * D;
     }
-    for (int d = 0; d < D; d++) out[d] += p * ld(vp, a->dtype, v_off + d);
+    for (int d = 0; d < D; d++) out[d] += p * (a->vs * ld(vp, a->dtype, v_off + d));
   }
   for (int d = 0; d < D; d++) out[d] /= l;
 }
@@ -118,7 +138,9 @@ static void attend_row(const dgo_args* a, int b, int i, int h, double* scores, d
 static int check(const dgo_args* a) {
   if (a->B < 0 || a->Nc <= 0 || a->Hq <= 0 || a->Hkv <= 0 || a->D <= 0) return -2;
   if (a->Hq % a->Hkv != 0) return -2;
-  if (a->dtype < DGO_BF16 || a->dtype > DGO_F64) return -3;
+  if (a->dtype < DGO_BF16 || a->dtype > DGO_FP8) return -3;
+  if (!(a->qs > 0) || !(a->ks > 0) || !(a->vs > 0) || isinf(a->qs) || isinf(a->ks) || isinf(a->vs))
+    return -2;
   for (int b = 0; b < a->B; b++)
     if (a->prefix_len[b] < 0 || a->prefix_len[b] > a->cap) return -4;
   return 0;
@@ -171,13 +193,15 @@ static int run(const dgo_args* a, int n_rows, const int32_t* rows, double* out) 
 /* Threads the parallel loops above use (the OpenMP default team size). */
 int dgo_num_threads(void) { return omp_get_max_threads(); }
 
-/* Canvas step: unmasked attention over [cache rows 0..L-1 ; canvas rows 0..Nc-1]. */
+/* Canvas step: unmasked attention over [cache rows 0..L-1 ; canvas rows 0..Nc-1].
+ * qs, ks, vs: per-tensor scales of the stored q, K and V values. */
 int dgo_canvas_attn(int dtype, int B, int Nc, int Hq, int Hkv, int D, double scale,
                     const void* q, const void* k_cache, const void* v_cache, int64_t cap,
                     const int32_t* prefix_len, const void* k_canvas, const void* v_canvas,
-                    int n_rows, const int32_t* rows, double* out) {
+                    int n_rows, const int32_t* rows, double* out, double qs, double ks,
+                    double vs) {
   dgo_args a = {dtype, B, Nc, Hq, Hkv, D, scale, q, k_cache, v_cache, cap, prefix_len,
-                k_canvas, v_canvas, 0};
+                k_canvas, v_canvas, 0, qs, ks, vs};
   return run(&a, n_rows, rows, out);
 }
 
@@ -185,9 +209,10 @@ int dgo_canvas_attn(int dtype, int B, int Nc, int Hq, int Hkv, int D, double sca
 int dgo_commit_attn(int dtype, int B, int Nc, int Hq, int Hkv, int D, double scale,
                     const void* q_blk, const void* k_cache, const void* v_cache, int64_t cap,
                     const int32_t* prefix_len, const void* k_blk, const void* v_blk,
-                    int n_rows, const int32_t* rows, double* out) {
+                    int n_rows, const int32_t* rows, double* out, double qs, double ks,
+                    double vs) {
   dgo_args a = {dtype, B, Nc, Hq, Hkv, D, scale, q_blk, k_cache, v_cache, cap, prefix_len,
-                k_blk, v_blk, 1};
+                k_blk, v_blk, 1, qs, ks, vs};
   return run(&a, n_rows, rows, out);
 }
 
@@ -198,7 +223,7 @@ int dgo_commit_attn(int dtype, int B, int Nc, int Hq, int Hkv, int D, double sca
 int dgo_append_block(int dtype, int B, int Nc, int Hkv, int D, const void* k_blk,
                      const void* v_blk, void* k_cache, void* v_cache, int64_t cap,
                      const int32_t* prefix_len) {
-  if (dtype < DGO_BF16 || dtype > DGO_F64) return -3;
+  if (dtype < DGO_BF16 || dtype > DGO_FP8) return -3;
   const size_t es = elem_size(dtype);
   const size_t row = (size_t)Hkv * D * es;
   for (int b = 0; b < B; b++) {
