@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # it is reported only while the source still matches.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "canvas_attn_l8k_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
-                  for f in ("dg_attn_bf16.hip", "dg_internal.h")]
+                  for f in ("dg_attn_mfma.hip", "dg_internal.h")]
 
 
 def kernel_source_hash():

@@ -52,7 +52,15 @@ int device_cu_count() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-size_t elem_size(int dtype) { return dtype == DG_BF16 ? 2 : 4; }
+// Bytes of one stored input element (q, K, V) and of one output / partial element.
+size_t elem_size(int dtype) { return dtype == DG_FP8 ? 1 : dtype == DG_BF16 ? 2 : 4; }
+size_t out_elem_size(int dtype) { return dtype == DG_F32 ? 4 : 2; }
+
+// The matrix-core kernels (bf16 and fp8) against the fp32 vector kernel.
+bool mfma_path(int dtype) { return dtype != DG_F32; }
+
+// Keys per chunk of the kernel a dtype runs on: split boundaries are multiples of it.
+int key_granule(int dtype) { return dtype == DG_FP8 ? 64 : dg::kKeyGranule; }
 
 // bf16 kernel shape for a call: DG_VARIANT=0..2 forces one for head_dim 128
 // (for tuning); otherwise the default shape.  head_dim 64 has one shape.
@@ -67,13 +75,14 @@ int bf16_variant(int head_dim) {
 }
 
 int rows_per_unit(int dtype, int variant) {
+  if (dtype == DG_FP8) return dg::variant_rows(dg::kVariantR128);
   return dtype == DG_BF16 ? dg::variant_rows(variant) : dg::kRowsF32;
 }
 
 dg_status check_shape(const dg_shape* s) {
   if (!s) return fail(DG_ERR_NULL, "shape is NULL");
-  if (s->dtype != DG_BF16 && s->dtype != DG_F32)
-    return fail(DG_ERR_DTYPE, "unknown dtype %d (DG_BF16=0, DG_F32=1)", s->dtype);
+  if (s->dtype != DG_BF16 && s->dtype != DG_F32 && s->dtype != DG_FP8)
+    return fail(DG_ERR_DTYPE, "unknown dtype %d (DG_BF16=0, DG_F32=1, DG_FP8=2)", s->dtype);
   if (s->batch < 1 || s->batch > DG_MAX_BATCH)
     return fail(DG_ERR_SHAPE, "batch %d outside 1..%d", s->batch, DG_MAX_BATCH);
   if (s->n_canvas != DG_N_CANVAS)
@@ -86,31 +95,43 @@ dg_status check_shape(const dg_shape* s) {
     return fail(DG_ERR_SHAPE, "head_dim %d, must be 64 or 128", s->head_dim);
   if (!(s->scale == s->scale) || isinf(s->scale))
     return fail(DG_ERR_SHAPE, "scale is not finite");
+  if (s->dtype == DG_FP8) {
+    if (s->head_dim != 128)
+      return fail(DG_ERR_SHAPE, "head_dim %d, DG_FP8 supports 128 only", s->head_dim);
+    const float sc[3] = {s->q_scale, s->k_scale, s->v_scale};
+    for (float x : sc)
+      if (!(x == x) || isinf(x)) return fail(DG_ERR_SHAPE, "an fp8 tensor scale is not finite");
+  }
   return DG_OK;
 }
+
+// Per-tensor scale of an fp8 tensor: <= 0 selects 1.
+float tensor_scale(float x) { return x > 0.f ? x : 1.f; }
 
 float effective_scale(const dg_shape* s) {
   return s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
 }
 
 // Keys per split forced through the environment (tests use it to exercise many
-// splits and ragged split ends); 0 when unset.
-int forced_split_keys() {
+// splits and ragged split ends), rounded up to the dtype's key granule; 0 when
+// unset.
+int forced_split_keys(int dtype) {
   const char* e = getenv("DG_SPLIT_KEYS");
   if (!e || !*e) return 0;
   const long v = strtol(e, nullptr, 10);
   if (v <= 0) return 0;
-  return (int)(((v + dg::kKeyGranule - 1) / dg::kKeyGranule) * dg::kKeyGranule);
+  const int g = key_granule(dtype);
+  return (int)(((v + g - 1) / g) * g);
 }
 
-// Target number of units: one workgroup per CU for the bf16 kernel (4 waves,
-// one per SIMD), one wave per SIMD for the fp32 kernel.
-int target_units(int dtype) { return device_cu_count() * (dtype == DG_BF16 ? 1 : 4); }
+// Target number of units: one workgroup per CU for the matrix-core kernels
+// (eight waves, two per SIMD), one wave per SIMD for the fp32 kernel.
+int target_units(int dtype) { return device_cu_count() * (mfma_path(dtype) ? 1 : 4); }
 
 // Split-key plan: every unit of every sequence gets about the same number of
 // keys, chosen so that the units fill the device about once.
 void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
-  const int variant = bf16_variant(s->head_dim);
+  const int variant = s->dtype == DG_FP8 ? dg::kVariantR128 : bf16_variant(s->head_dim);
   const int R = rows_per_unit(s->dtype, variant);
   const int G = s->n_heads_q / s->n_heads_kv;
   const int NRT = dg::kCanvas * G / R;
@@ -118,10 +139,11 @@ void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
   int64_t W = 0;
   for (int b = 0; b < s->batch; b++) W += (int64_t)(prefix_len[b] + dg::kCanvas) * per_split;
   const int T = target_units(s->dtype);
+  const int gran = key_granule(s->dtype);
   int64_t kappa = (W + T - 1) / T;
-  kappa = ((kappa + dg::kKeyGranule - 1) / dg::kKeyGranule) * dg::kKeyGranule;
-  kappa = std::max<int64_t>(kappa, s->dtype == DG_BF16 ? 256 : 64);
-  const int forced = forced_split_keys();
+  kappa = ((kappa + gran - 1) / gran) * gran;
+  kappa = std::max<int64_t>(kappa, mfma_path(s->dtype) ? 256 : 64);
+  const int forced = forced_split_keys(s->dtype);
   if (forced) kappa = forced;
   memset(p, 0, sizeof *p);
   p->batch = s->batch;
@@ -136,7 +158,7 @@ void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
     const int64_t K = (int64_t)prefix_len[b] + dg::kCanvas;
     int S = (int)((K + kappa - 1) / kappa);
     int64_t sk = (K + S - 1) / S;
-    sk = ((sk + dg::kKeyGranule - 1) / dg::kKeyGranule) * dg::kKeyGranule;
+    sk = ((sk + gran - 1) / gran) * gran;
     S = (int)((K + sk - 1) / sk);
     p->seq[b].prefix_len = prefix_len[b];
     p->seq[b].n_splits = S;
@@ -151,7 +173,7 @@ void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
 
 // Bytes of one partial row: the normalised output (bf16 or fp32) plus max and sum.
 size_t partial_row_bytes(const dg_shape* s) {
-  return (size_t)s->head_dim * elem_size(s->dtype) + 2 * sizeof(float);
+  return (size_t)s->head_dim * out_elem_size(s->dtype) + 2 * sizeof(float);
 }
 
 size_t plan_workspace(const dg_shape* s, const Plan& p) {
@@ -248,21 +270,27 @@ dg_status prepare(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
   a.part_o = workspace;
   a.part_ml = workspace ? (float*)((char*)workspace + (size_t)c->plan.n_units *
                                                            c->plan.rows_per_unit *
-                                                           shape->head_dim * elem_size(shape->dtype))
+                                                           shape->head_dim * out_elem_size(shape->dtype))
                         : nullptr;
   a.cap = kv_cache->capacity;
   a.n_heads_q = shape->n_heads_q;
   a.n_heads_kv = shape->n_heads_kv;
   a.scale_log2 = effective_scale(shape) * 1.4426950408889634f;
+  a.out_scale = 1.f;
+  if (shape->dtype == DG_FP8) {
+    a.scale_log2 *= tensor_scale(shape->q_scale) * tensor_scale(shape->k_scale);
+    a.out_scale = tensor_scale(shape->v_scale);
+  }
   return DG_OK;
 }
 
 dg_status launch(const Call& c, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  const bool bf16 = c.shape.dtype == DG_BF16;
+  const int dt = c.shape.dtype;
   time_begin(0, st);
-  int err = bf16 ? dg::launch_attn_bf16(c.args, c.plan, c.shape.head_dim, c.causal, stream)
-                 : dg::launch_attn_f32(c.args, c.plan, c.shape.head_dim, c.causal, stream);
+  int err = dt == DG_BF16  ? dg::launch_attn_bf16(c.args, c.plan, c.shape.head_dim, c.causal, stream)
+            : dt == DG_FP8 ? dg::launch_attn_fp8(c.args, c.plan, c.causal, stream)
+                           : dg::launch_attn_f32(c.args, c.plan, c.shape.head_dim, c.causal, stream);
   time_end(0, st);
   if (err != 0)
     return fail(DG_ERR_HIP, "attention kernel launch failed: %s",
@@ -271,14 +299,14 @@ dg_status launch(const Call& c, void* stream) {
   for (int b = 0; b < c.plan.batch; b++) any = any || c.plan.seq[b].n_splits > 1;
   if (any) {
     time_begin(1, st);
-    err = dg::launch_merge(c.args, c.plan, c.shape.head_dim, bf16, stream);
+    err = dg::launch_merge(c.args, c.plan, c.shape.head_dim, dt != DG_F32, stream);
     time_end(1, st);
     if (err != 0)
       return fail(DG_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString((hipError_t)err));
   }
   if (getenv("DG_LOG")) {
-    fprintf(stderr, "[dg] %s variant=%d units=%d R=%d NRT=%d", c.causal ? "commit" : "canvas",
-            c.plan.variant, c.plan.n_units, c.plan.rows_per_unit, c.plan.n_rowtiles);
+    fprintf(stderr, "[dg] %s dtype=%d variant=%d units=%d R=%d NRT=%d", c.causal ? "commit" : "canvas",
+            dt, c.plan.variant, c.plan.n_units, c.plan.rows_per_unit, c.plan.n_rowtiles);
     for (int b = 0; b < c.plan.batch; b++)
       fprintf(stderr, " | b%d L=%d S=%d keys/split=%d", b, c.plan.seq[b].prefix_len,
               c.plan.seq[b].n_splits, c.plan.seq[b].split_keys);
@@ -296,11 +324,11 @@ size_t dg_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len) {
     return 0;
   // The natural plan never exceeds T + B*Hkv*NRT units whatever the prefixes;
   // the bound in bytes is largest for the widest row tile.
-  const int R = shape->dtype == DG_BF16 ? dg::variant_rows(dg::kVariantR256) : dg::kRowsF32;
+  const int R = mfma_path(shape->dtype) ? dg::variant_rows(dg::kVariantR256) : dg::kRowsF32;
   const int G = shape->n_heads_q / shape->n_heads_kv;
   const int NRT = dg::kCanvas * G / R;
   int64_t units = (int64_t)target_units(shape->dtype) + (int64_t)shape->batch * shape->n_heads_kv * NRT;
-  const int forced = forced_split_keys();
+  const int forced = forced_split_keys(shape->dtype);
   if (forced) {
     const int64_t S = (max_prefix_len + dg::kCanvas + forced - 1) / forced;
     units = std::max<int64_t>(units, S * shape->batch * shape->n_heads_kv * NRT);
@@ -338,16 +366,16 @@ dg_status dg_canvas_step_loop(const dg_shape* shape, int32_t n_steps, const void
   dg_status st = prepare(shape, q, kv_cache, prefix_len, kv_canvas, out, workspace, ws_bytes,
                          false, &c);
   if (st) return st;
-  const size_t es = elem_size(shape->dtype);
+  const size_t es = elem_size(shape->dtype), eo = out_elem_size(shape->dtype);
   if (((q_step_stride * (int64_t)es) & 15) || ((kv_step_stride * (int64_t)es) & 15) ||
-      ((out_step_stride * (int64_t)es) & 15))
+      ((out_step_stride * (int64_t)eo) & 15))
     return fail(DG_ERR_ALIGN, "step strides must keep 16-byte alignment");
   for (int s = 0; s < n_steps; s++) {
     Call cs = c;
     cs.args.q = (const char*)q + (int64_t)s * q_step_stride * es;
     cs.args.k_new = (const char*)kv_canvas->k + (int64_t)s * kv_step_stride * es;
     cs.args.v_new = (const char*)kv_canvas->v + (int64_t)s * kv_step_stride * es;
-    cs.args.out = (char*)out + (int64_t)s * out_step_stride * es;
+    cs.args.out = (char*)out + (int64_t)s * out_step_stride * eo;
     st = launch(cs, stream);
     if (st) return st;
   }

@@ -1,4 +1,5 @@
-// dg_attn_bf16.hip -- split-key canvas / commit attention, bf16 in, fp32 accumulate (gfx950).
+// dg_attn_mfma.hip -- split-key canvas / commit attention on the matrix cores (gfx950):
+// bf16 in, or e4m3 (fp8) in; fp32 accumulate; bf16 out.
 //
 // Computes, for one work unit (sequence b, kv head g, key split s, row tile rt),
 // softmax attention of R packed query rows against the unit's keys, where the
@@ -13,7 +14,7 @@
 // Design (CDNA4):
 //   * A workgroup is eight wave64s = WM row groups x WK key groups; each wave
 //     owns 32 packed query rows (its Q operands stay in VGPRs) and walks its key
-//     group's 32-key chunks.
+//     group's chunks (32 keys in bf16, 64 in fp8).
 //   * GQA packing: the G query heads of kv head g are rows p = i*G + hh of one
 //     256*G-row matrix, so every K/V tile read from LDS feeds all query heads of
 //     the group at once.
@@ -32,7 +33,7 @@
 //     matrix pipe and the vector ALU work at the same time.  The MFMA phase runs
 //     at raised wave priority.
 //   * K/V stream HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a
-//     ring of NSLOT stages (one 32-key tile per key group each); a stage is
+//     ring of NSLOT stages (one chunk of K and V per key group each); a stage is
 //     refilled as soon as the barrier after its last operand read has passed,
 //     which keeps NSLOT-2 chunks of loads in flight.  Whole tiles inside the
 //     cache or the canvas use a scalar base plus precomputed 32-bit lane offsets;
@@ -51,8 +52,17 @@
 //     writes its normalised rows (bf16) plus (max, sum) as a partial, or the final
 //     output when the sequence has a single split, through an LDS staging area so
 //     that every store is a whole 128-byte row segment.
+//
+// The fp8 format (OCP e4m3 queries, keys and values with per-tensor scales) runs
+// the same kernel with v_mfma_f32_32x32x64_f8f6f4: a chunk is 64 keys (the same
+// 8 KB per K or V tile as 32 bf16 keys at head_dim 128), the scores of its two
+// 32-key halves feed one value MFMA per 32 head_dim rows, and the exponentials
+// are rounded to e4m3 for it.  Its differences are kept in FmtFp8 and the
+// overloads taking fp8 operands below.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "dg_internal.h"
 
@@ -63,9 +73,52 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kRescaleThreshold = 64.f;  // log2 units
+
+// Element formats of the ping-pong kernel.  A chunk is the run of keys a wave
+// takes per step; both formats move 8 KB of K and 8 KB of V per chunk at
+// head_dim 128.  The exponentials of a chunk run up to 2^(kBias + kThreshold)
+// relative to the reference max (the lazy rescale below).
+struct FmtBf16 {
+  static constexpr int ESZ = 2;              // bytes per element
+  static constexpr int TK = 32;              // keys per chunk
+  static constexpr float kThreshold = 64.f;  // rescale when a chunk max rises this far (log2)
+  static constexpr float kBias = 0.f;        // exponent offset of the exponentials
+};
+// e4m3 tops out at 448 (just under 2^8.81), and the gfx950 conversion returns NaN
+// rather than saturating from 464 up, so the exponentials that become the B
+// operand of the value MFMA must stay below that: a bias of 5 plus a threshold of
+// 3.5 bounds them by 2^8.5.  The bias also lifts the bulk of a diffuse row (2^-6 ..
+// 2^-10 of its max) into e4m3's normal range, where the rounding error is 2^-4
+// relative; values below 2^-11 of the reference become subnormal and carry a
+// negligible weight.
+struct FmtFp8 {
+  static constexpr int ESZ = 1;
+  static constexpr int TK = 64;
+  static constexpr float kThreshold = 3.5f;
+  static constexpr float kBias = 5.f;
+};
+template <class F>
+constexpr bool is_fp8 = F::ESZ == 1;
+
+// fp8 rows are 128 bytes, eight 16-byte chunks; logical chunk c of row r is
+// stored at physical chunk c ^ swz8(r).  Per cycle the score operand reads take
+// one logical chunk of 16 rows {0-7, 16-23} or {8-15, 24-31} of a 32-row half
+// (the permuted key rows of kperm8) and the transposing V reads 8 consecutive
+// rows of two adjacent chunks: both land on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz8(int r) { return 2 * ((r >> 1) & 3) | ((r >> 4) & 1); }
+
+// Key row that fp8 score MFMA row i (0..31) reads within its 32-key half.  The
+// MFMA leaves row i of its result in lane half (i / 4) % 2, register 4(i / 8) +
+// i % 4; with this permutation lane half h holds keys 16h .. 16h+15 in register
+// order, so the e4m3 exponentials of a 64-key chunk are bytes 16t + i = key
+// 32t + 16h + i, which two 8-row transposing reads match on the V side.
+__device__ __forceinline__ int kperm8(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
   // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
@@ -179,7 +232,7 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 }
 
 // This wave's share of the global_load_lds instructions that fill one ring stage.
-// A stage holds, for every key group kt, a 32-key K tile and a 32-key V tile; the
+// A stage holds, for every key group kt, one chunk of K and V (F::TK keys); the
 // K tiles of the stage are consecutive in LDS and so are its V tiles, so each
 // half is a run of 1 KB blocks (block b: keys b*RPI .. b*RPI+RPI-1 of the stage).
 // Waves 0 .. NW/2-1 fill the K half and the others the V half, each GPW
@@ -189,8 +242,8 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 // Writing M0 before every load would stall the wave at each of them.
 // Each load moves 1 KB: lane l writes 16 bytes at 16*l of its block, i.e. block
 // row l / CH, physical chunk l % CH, and fetches the logical chunk that the
-// swizzle stores there (K: chunk ^ (row % CH); V: chunk ^ 4*(row % 4), row
-// within the tile).  Everything that does not depend on the stage is computed
+// swizzle stores there (bf16 K: chunk ^ (row % CH); bf16 V: chunk ^ 4*(row % 4);
+// fp8 K and V: chunk ^ swz8(row); row within the tile).  Everything that does not depend on the stage is computed
 // once per wave; per stage only the byte offset of its first key is formed, and
 // a stage lying wholly in the cache or wholly in the canvas (every stage but the
 // one at the seam and the unit's last) is issued as scalar base + 32-bit lane
@@ -200,10 +253,10 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 // so that every operand read is a per-lane base plus an immediate offset.
 constexpr uint32_t kVRegion = 65536;
 
-template <int D, int WK, int NW = 8>
+template <class F, int D, int WK, int NW = 8>
 struct StageLoads {
-  static constexpr int CH = D / 8, ROWB = D * 2, RPI = 1024 / ROWB, IPT = 32 / RPI;
-  static constexpr int TILEB = 32 * ROWB, GPW = WK * 2 * IPT / NW;
+  static constexpr int ROWB = D * F::ESZ, CH = ROWB / 16, RPI = 1024 / ROWB, IPT = F::TK / RPI;
+  static constexpr int TILEB = F::TK * ROWB, GPW = WK * 2 * IPT / NW;
   static_assert(NW % 2 == 0 && GPW * NW == WK * 2 * IPT && GPW >= 1 && GPW <= 4,
                 "whole blocks per wave, instruction offsets below 4 KB");
   uint64_t cb;              // cache K or V base of (sequence, kv head)
@@ -215,11 +268,11 @@ struct StageLoads {
   int32_t rsb, L, kstop;
 };
 
-template <int D, int WK, int NW>
-__device__ __forceinline__ void stage_loads_init(StageLoads<D, WK, NW>& sl, const char* kc,
+template <class F, int D, int WK, int NW>
+__device__ __forceinline__ void stage_loads_init(StageLoads<F, D, WK, NW>& sl, const char* kc,
                                                  const char* vc, const char* kn, const char* vn,
                                                  int rsb, int L, int kstop, int wave, int lane) {
-  using SL = StageLoads<D, WK, NW>;
+  using SL = StageLoads<F, D, WK, NW>;
   const int lr = lane / SL::CH, lp = lane % SL::CH;
   sl.rsb = rsb;
   sl.L = L;
@@ -237,7 +290,7 @@ __device__ __forceinline__ void stage_loads_init(StageLoads<D, WK, NW>& sl, cons
 #pragma unroll
   for (int e = 0; e < SL::GPW; e++) {
     const int r = ((b0 + e) % SL::IPT) * SL::RPI + lr;  // row within the tile
-    const int sw = isv ? ((4 * (r & 3)) & (SL::CH - 1)) : (r & (SL::CH - 1));
+    const int sw = is_fp8<F> ? swz8(r) : isv ? ((4 * (r & 3)) & (SL::CH - 1)) : (r & (SL::CH - 1));
     sl.lane[e] = (uint32_t)(e * SL::RPI + lr) * (uint32_t)rsb + 16u * (uint32_t)(lp ^ sw) -
                  1024u * (uint32_t)e;
   }
@@ -246,9 +299,9 @@ __device__ __forceinline__ void stage_loads_init(StageLoads<D, WK, NW>& sl, cons
 // Where the keys of the stage from skey0 come from: 1 wholly the cache, 2 wholly
 // the canvas (both issued as scalar base + lane offsets), 0 both or past the
 // unit's end (rows formed per lane).
-template <int D, int WK, int NW>
-__device__ __forceinline__ int stage_source(int skey0, const StageLoads<D, WK, NW>& sl) {
-  const int send = skey0 + 32 * WK;
+template <class F, int D, int WK, int NW>
+__device__ __forceinline__ int stage_source(int skey0, const StageLoads<F, D, WK, NW>& sl) {
+  const int send = skey0 + F::TK * WK;
   if (send <= sl.L && send <= sl.kstop) return 1;
   if (skey0 >= sl.L && send <= sl.kstop) return 2;
   return 0;
@@ -283,9 +336,9 @@ __device__ __forceinline__ void gll_block(const char* sb, const uint32_t* vo, ui
 // slot.  Tiles past the unit's last key are loaded too (rows clamped onto the
 // unit's last key) so that each wave always has the same number of loads per
 // stage in flight.
-template <int D, int WK, int NW>
-__device__ __forceinline__ void issue_stage(uint32_t slot, int skey0, const StageLoads<D, WK, NW>& sl) {
-  using SL = StageLoads<D, WK, NW>;
+template <class F, int D, int WK, int NW>
+__device__ __forceinline__ void issue_stage(uint32_t slot, int skey0, const StageLoads<F, D, WK, NW>& sl) {
+  using SL = StageLoads<F, D, WK, NW>;
   constexpr int G = SL::GPW;
   const int src = stage_source(skey0, sl);
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + sl.dst);
@@ -448,11 +501,233 @@ __device__ __forceinline__ void values(const bf16x8 (&vop)[MB][2], const bf16x8 
   values<MB>(vop, pb, acc.o);
 }
 
+// The bf16 registers as one group, so that the kernel body below is written
+// once for both formats.
+template <int D>
+struct Ops16 {
+  bf16x8 q[D / 16];     // B operands of S^T = K Q^T: lane (n, h), k-step ks holds
+                        // q[row][D/2*h + 8*ks .. +8] (the head_dim order the K operands use)
+  bf16x8 k[D / 16];     // K operands for the next score MFMAs
+  bf16x8 v[D / 32][2];  // V^T operands for the next value MFMAs
+  bf16x8 p[2];          // packed exponentials for the next value MFMAs
+  f32x16 s[1];          // scores of the chunk the next softmax works on
+};
+
+template <int D>
+__device__ __forceinline__ void load_k_operands(const uint32_t (&kbase)[D / 16], uint32_t off, Ops16<D>& op) {
+  load_k_operands<D>(kbase, off, op.k);
+}
+template <int D>
+__device__ __forceinline__ void scores(Ops16<D>& op) { scores<D>(op.k, op.q, op.s[0]); }
+template <int D>
+__device__ __forceinline__ void load_v_operands(const uint32_t (&vbase)[D / 32], uint32_t off, Ops16<D>& op) {
+  load_v_operands<D>(vbase, off, op.v);
+}
+template <int MB, bool CAUSAL, int D>
+__device__ __forceinline__ void prepare_scores(Ops16<D>& op, bool masked, int key0, int kstop, int L,
+                                               int qi, int h, float c2, State<MB>& acc) {
+  prepare_scores<MB, CAUSAL>(op.s[0], masked, key0, kstop, L, qi, h, c2, acc);
+}
+template <int MB, int D>
+__device__ __forceinline__ void numerators(Ops16<D>& op, float c2, State<MB>& acc) {
+  numerators<MB>(op.s[0], c2, acc, op.p);
+}
+template <int MB, int D>
+__device__ __forceinline__ void values(const Ops16<D>& op, State<MB>& acc) {
+  values<MB>(op.v, op.p, acc);
+}
+
+// ---------------------------------------------------------------------------
+// fp8 operands.  v_mfma_f32_32x32x64_f8f6f4 multiplies byte j of A lane (i, h)
+// with byte j of B lane (n, h) (lane = i + 32h) and sums over h and j, so any
+// assignment of head_dim (or of keys) to (h, j) works as long as both operands
+// use the same one; the result has the 32x32 layout of the bf16 MFMA.
+
+// e4m3 x e4m3 (format code 0 for both operands), no block scales
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Per-lane LDS offsets of the fp8 operand reads (head_dim 128): a 64-key chunk
+// is two 32-key halves t of 32 * 128 bytes, and a transposing V read covers 8
+// rows, so halves and 8-row blocks are immediate offsets of 4096 and 1024.
+struct LaneOffsets8 {
+  uint32_t k[2][2];  // K row kperm8(n), logical chunk 4ks + 2h + part (ds_read_b128)
+  uint32_t q[2][2];  // query row n, same chunks
+  uint32_t v[4];     // ds_read_b64_tr_b8 of head_dim block mb, row 16h + (lane%16)/2
+};
+
+__device__ __forceinline__ LaneOffsets8 lane_offsets8(int lane) {
+  LaneOffsets8 o;
+  const int n = lane & 31, h = lane >> 5, kr = kperm8(n);
+#pragma unroll
+  for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+    for (int part = 0; part < 2; part++) {
+      const int c = 4 * ks + 2 * h + part;
+      o.k[ks][part] = kr * 128 + 16 * (c ^ swz8(kr));
+      o.q[ks][part] = n * 128 + 16 * (c ^ swz8(n));
+    }
+  // transposing read: in each 16-lane group, lane 2e + b supplies bytes 8b .. 8b+7
+  // of the group's 16 columns in row e, and lane i receives column i of the 8 rows
+  const int i16 = lane & 15, e = i16 >> 1, row = 16 * h + e;
+#pragma unroll
+  for (int mb = 0; mb < 4; mb++) {
+    const int c = 2 * mb + ((lane >> 4) & 1);
+    o.v[mb] = row * 128 + 16 * (c ^ swz8(row)) + 8 * (i16 & 1);
+  }
+  return o;
+}
+
+// Registers of the fp8 pipeline (head_dim 128).
+struct Ops8 {
+  i32x8 q[2];     // B operands of S^T = K Q^T: lane (n, h), k-step ks holds bytes
+                  // 64ks + 32h .. +32 of query row n
+  i32x8 k[2][2];  // A operands [half t][k-step]: the same bytes of key row 32t + kperm8(n)
+  i32x8 v[4];     // A operands of O^T += V^T P^T: lane (d, h), byte 16t + i holds
+                  // V[32t + 16h + i][32mb + d]
+  i32x8 p;        // B operand: lane (n, h), byte 16t + i holds the e4m3 exponential of
+                  // query n and key 32t + 16h + i
+  f32x16 s[2];    // scores of the chunk the next softmax works on, per half
+};
+
+// two 16-byte LDS reads joined into one 32-byte operand
+__device__ __forceinline__ i32x8 lds_read_2x16(uint32_t a0, uint32_t a1) {
+  const i32x4 lo = *(const LDS_AS i32x4*)(uintptr_t)a0;
+  const i32x4 hi = *(const LDS_AS i32x4*)(uintptr_t)a1;
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ void load_k_operands(const uint32_t (&kbase)[2][2], uint32_t off, Ops8& op) {
+#pragma unroll
+  for (int t = 0; t < 2; t++)
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+      op.k[t][ks] = lds_read_2x16(kbase[ks][0] + off + 4096u * t, kbase[ks][1] + off + 4096u * t);
+}
+
+__device__ __forceinline__ void scores(Ops8& op) {
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) op.s[t][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) op.s[t] = mfma_f8(op.k[t][ks], op.q[ks], op.s[t]);
+  }
+}
+
+__device__ __forceinline__ void load_v_operands(const uint32_t (&vbase)[4], uint32_t off, Ops8& op) {
+#pragma unroll
+  for (int mb = 0; mb < 4; mb++) {
+    const uint32_t a = vbase[mb] + off;
+    i32x2 r[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++)  // (half, 8-row block) = (j / 2, j % 2)
+      r[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (LDS_AS i32x2*)(uintptr_t)(a + 4096u * (j >> 1) + 1024u * (j & 1)));
+    op.v[mb] = (i32x8){r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+  }
+}
+
+// Max of the 32 scores of a lane: one v_max3 chain split over two asm blocks (an
+// asm statement takes at most 30 operands).
+__device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
+  float m;
+  asm("v_max3_f32 %0, %1, %2, %3\n\t"
+      "v_max3_f32 %0, %0, %4, %5\n\t"
+      "v_max3_f32 %0, %0, %6, %7\n\t"
+      "v_max3_f32 %0, %0, %8, %9\n\t"
+      "v_max3_f32 %0, %0, %10, %11\n\t"
+      "v_max3_f32 %0, %0, %12, %13\n\t"
+      "v_max3_f32 %0, %0, %14, %15\n\t"
+      "v_max3_f32 %0, %0, %16, %17\n\t"
+      "v_max3_f32 %0, %0, %18, %19\n\t"
+      "v_max3_f32 %0, %0, %20, %21\n\t"
+      "v_max3_f32 %0, %0, %22, %23\n\t"
+      "v_max3_f32 %0, %0, %24, %25\n\t"
+      "v_max3_f32 %0, %0, %26, %27"
+      : "=&v"(m)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+        "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+        "v"(a[14]), "v"(a[15]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]),
+        "v"(b[5]), "v"(b[6]), "v"(b[7]), "v"(b[8]), "v"(b[9]), "v"(b[10]));
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3\n\t"
+      "v_max3_f32 %0, %0, %4, %5\n\t"
+      "v_max_f32 %0, %0, %6"
+      : "=&v"(r)
+      : "v"(m), "v"(b[11]), "v"(b[12]), "v"(b[13]), "v"(b[14]), "v"(b[15]));
+  return r;
+}
+
+// fp8 counterpart of prepare_scores: masking with the permuted key order, the
+// max of the chunk's 32 scores, and the lazy rescale with the exponent bias.
+template <int MB, bool CAUSAL>
+__device__ __forceinline__ void prepare_scores(Ops8& op, bool masked, int key0, int kstop, int L,
+                                               int qi, int h, float c2, State<MB>& acc) {
+  if (masked) {
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int key = key0 + 32 * t + 16 * h + i;
+        bool ok = key < kstop;
+        if (CAUSAL) ok = ok && (key < L || key - L <= qi);
+        op.s[t][i] = ok ? op.s[t][i] : -INFINITY;
+      }
+  }
+  const float m = max32(op.s[0], op.s[1]);
+  if (__any(m > acc.thr)) {
+    const float mnew = fmaxf(acc.mlog, partner_max(m * c2) - FmtFp8::kBias);
+    const float alpha = __builtin_amdgcn_exp2f(acc.mlog - mnew);
+    acc.mlog = mnew;
+    acc.thr = (mnew + (FmtFp8::kBias + FmtFp8::kThreshold)) / c2;
+    acc.lsum *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc.o[mb][i] *= alpha;
+  }
+}
+
+// exp2(s*c - m) of the 64 keys, summed in fp32 before rounding and packed to
+// e4m3 (v_cvt_pk_fp8_f32 writes two bytes, round to nearest even) in key order.
+template <int MB>
+__device__ __forceinline__ void numerators(Ops8& op, float c2, State<MB>& acc) {
+  const float nm = -acc.mlog;
+#pragma unroll
+  for (int t = 0; t < 2; t++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) op.s[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(op.s[t][i], c2, nm));
+  float part[8];
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    const f32x16& x = op.s[q >> 2];
+    const int b = 4 * (q & 3);
+    part[q] = (x[b] + x[b + 1]) + (x[b + 2] + x[b + 3]);
+  }
+  acc.lsum += ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+#pragma unroll
+  for (int w = 0; w < 8; w++) {
+    const f32x16& x = op.s[w >> 2];
+    const int b = 4 * (w & 3);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[b], x[b + 1], 0, false);
+    op.p[w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[b + 2], x[b + 3], lo, true);
+  }
+}
+
+template <int MB>
+__device__ __forceinline__ void values(const Ops8& op, State<MB>& acc) {
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++) acc.o[mb] = mfma_f8(op.v[mb], op.p, acc.o[mb]);
+}
+
 // The kernel.  Wave (rg, kg) processes chunk k = tile k*WK + kg of the unit for
 // k = 0 .. nstages-1; chunk k lives in ring stage k (slot k mod NSLOT).  Per chunk
 // a wave runs
-//   X(k): requests stage k+NSLOT, O += V(k) P(k) (8 MFMAs), S(k+1) = K(k+1) Q^T
-//         (8 MFMAs) with the V(k+1) operand reads between them
+//   X(k): requests stage k+NSLOT, O += V(k) P(k) (bf16: 8 MFMAs, fp8: 4),
+//         S(k+1) = K(k+1) Q^T (bf16: 8 MFMAs, fp8: 4) with the V(k+1) operand
+//         reads between them
 //   Y(k): K(k+2) operand reads, softmax of S(k+1) -> P(k+1)
 // One workgroup barrier per chunk: barrier k follows Y(k) in waves 0-3 (group 0)
 // and X(k) in waves 4-7 (group 1), so group 1 runs half a chunk behind and, on
@@ -467,18 +742,23 @@ __device__ __forceinline__ void values(const bf16x8 (&vop)[MB][2], const bf16x8 
 // is requested only after the prologue (its slot holds the queries until then),
 // yet group 0 reads K(2) in Y(0); one extra barrier E, after group 0's X(0) and
 // before group 1's X(0), waits for it.
-template <int D, bool CAUSAL, int WM, int WK, int NSLOT>
-__global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan) {
+// One body serves both formats (F = FmtBf16 or FmtFp8); the entry points are
+// attn_bf16_kernel and attn_fp8_kernel below.
+template <class F, int D, bool CAUSAL, int WM, int WK, int NSLOT>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, const Plan& plan) {
   static_assert(WM * WK == 8, "eight waves: row groups x key groups");
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static_assert(!is_fp8<F> || D == 128, "fp8: head_dim 128");
   static_assert(NSLOT >= 4, "the ring keeps at least two stages in flight");
+  constexpr bool F8 = is_fp8<F>;
+  constexpr int TK = F::TK;             // keys per chunk
   constexpr int NT = 512;               // threads per workgroup
   constexpr int R = 32 * WM;            // packed rows per unit
-  constexpr int KS = D / 16;            // MFMA k-steps over head_dim
-  constexpr int CH = D / 8;             // 16-byte chunks per K/V row
+  constexpr int KS = D / 16;            // bf16 MFMA k-steps over head_dim
   constexpr int MB = D / 32;            // 32-row blocks of O^T
-  constexpr int ROWB = D * 2;           // bytes per K/V row
-  constexpr int TILEB = 32 * ROWB;      // bytes per 32-key K (or V) tile
+  constexpr int ROWB = D * F::ESZ;      // bytes per K/V row
+  constexpr int CH = ROWB / 16;         // 16-byte chunks per K/V row
+  constexpr int TILEB = TK * ROWB;      // bytes per chunk of K (or V)
   constexpr int SLOTB = WK * 2 * TILEB; // one ring stage: K and V tiles of every key group
   constexpr int GPW = SLOTB / 1024 / 8; // global_load_lds per wave per stage
   static_assert(GPW >= 1 && SLOTB % 8192 == 0, "stage load split");
@@ -486,6 +766,9 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
                                         // max, sum, padding to whole 16-byte words
   constexpr int MERGEB = (WK - 1) * WM * 64 * PER * 4;
   static_assert(MERGEB <= NSLOT * SLOTB, "key-group merge fits in the ring");
+  // score MFMAs per chunk and the V operand reads issued between them
+  constexpr int NSM = F8 ? 4 : KS, NVR = 4 * MB;
+  static_assert(NVR % NSM == 0, "V reads spread evenly over the score MFMAs");
   __shared__ __attribute__((aligned(1024))) char ring[NSLOT * SLOTB];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -503,14 +786,14 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
   if (CAUSAL) kend = min(kend, L + div_rcp(row0 + R - 1, plan.rcp_g) + 1);
   const int kbeg = u.s * sp.split_keys;
   const int kstop = min(kbeg + sp.split_keys, kend);
-  const int ntiles = kstop > kbeg ? (kstop - kbeg + 31) / 32 : 0;
+  const int ntiles = kstop > kbeg ? (kstop - kbeg + TK - 1) / TK : 0;
   const int nstages = (ntiles + WK - 1) / WK;
 
   const int64_t cap = a.cap;
-  const uint16_t* kc = (const uint16_t*)a.k_cache;
-  const uint16_t* vc = (const uint16_t*)a.v_cache;
-  const uint16_t* kn = (const uint16_t*)a.k_new;
-  const uint16_t* vn = (const uint16_t*)a.v_new;
+  const char* kc = (const char*)a.k_cache;
+  const char* vc = (const char*)a.v_cache;
+  const char* kn = (const char*)a.k_new;
+  const char* vn = (const char*)a.v_new;
 
   // ---- commit: append the block's K/V rows of head g to cache rows L..L+255
   if (CAUSAL && a.k_append != nullptr) {
@@ -522,22 +805,22 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
     for (int idx = tid; idx < 2 * per; idx += NT) {
       const int which = idx / per, rem = idx % per;
       const int r = r0 + rem / CH, c = rem % CH;
-      const int64_t src = ((int64_t)(u.b * kCanvas + r) * Hkv + u.g) * D + c * 8;
-      const int64_t dst = (((int64_t)u.b * cap + L + r) * Hkv + u.g) * D + c * 8;
+      const int64_t src = ((int64_t)(u.b * kCanvas + r) * Hkv + u.g) * ROWB + c * 16;
+      const int64_t dst = (((int64_t)u.b * cap + L + r) * Hkv + u.g) * ROWB + c * 16;
       const uint4 val = *(const uint4*)((which ? vn : kn) + src);
-      *(uint4*)((uint16_t*)(which ? a.v_append : a.k_append) + dst) = val;
+      *(uint4*)((char*)(which ? a.v_append : a.k_append) + dst) = val;
     }
   }
 
   const int prow = row0 + 32 * rg + n;  // packed row of this lane's scores
   const int qi = div_rcp(prow, plan.rcp_g);
 
-  StageLoads<D, WK, 8> sl;
-  stage_loads_init<D, WK, 8>(sl, (const char*)(kc + ((int64_t)u.b * cap * Hkv + u.g) * D),
-                          (const char*)(vc + ((int64_t)u.b * cap * Hkv + u.g) * D),
-                          (const char*)(kn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
-                          (const char*)(vn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
-                          Hkv * D * 2, L, kstop, wave, lane);
+  StageLoads<F, D, WK, 8> sl;
+  stage_loads_init<F, D, WK, 8>(sl, kc + ((int64_t)u.b * cap * Hkv + u.g) * ROWB,
+                                vc + ((int64_t)u.b * cap * Hkv + u.g) * ROWB,
+                                kn + ((int64_t)u.b * kCanvas * Hkv + u.g) * ROWB,
+                                vn + ((int64_t)u.b * kCanvas * Hkv + u.g) * ROWB,
+                                Hkv * ROWB, L, kstop, wave, lane);
   // The first two stages (the operands of the first chunk and the scores of the
   // second) are requested as soon as the unit is known; everything below overlaps
   // their flight.  Only these two precede the first wait: the compiler's wait for
@@ -550,10 +833,10 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
   // The unit's R query rows travel the same way, into ring space that stages 2..
   // take over only when the prologue ends: rows 0..QRH-1 at offset 32 KB of the K
   // region, the rest at the same offset of the V region, swizzled like a K tile
-  // (chunk ^ row % CH), so that each wave reads its B operands with the K operand
-  // offsets.  Loaded per lane straight into registers, every instruction would
-  // touch 64 cache lines (32 rows, 16 bytes of each), and both key groups would
-  // fetch the same rows.
+  // (bf16: chunk ^ row % CH; fp8: chunk ^ swz8(row)), so that each wave reads its
+  // B operands with conflict-free 16-byte reads.  Loaded per lane straight into
+  // registers, every instruction would touch 64 cache lines (32 rows, 16 bytes of
+  // each), and both key groups would fetch the same rows.
   constexpr int QRH = 32768 / ROWB;       // query rows per 32 KB half
   constexpr int QRW = R / 8;              // rows loaded per wave
   constexpr int QPW = QRW * ROWB / 1024;  // loads per wave
@@ -574,16 +857,20 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
       for (int e = 0; e < NB4; e++) {
         const int r = r_first + (j + e) * QRPI + lane / CH;  // row within the unit
         const int pr = row0 + r, qq = div_rcp(pr, plan.rcp_g);
-        const int c = (lane % CH) ^ (r % CH);                // logical chunk at this slot
+        const int c = (lane % CH) ^ (F8 ? swz8(r) : r % CH);  // logical chunk at this slot
         vo[e] = (uint32_t)((qq * Hq + pr - qq * G) * ROWB + 16 * c) - 1024u * (uint32_t)e;
       }
       gll_block<NB4>(qb, vo, __builtin_amdgcn_readfirstlane(q_lds(r_first + j * QRPI)));
     }
   }
   const int npre = min(2, nstages);
-  for (int st = 0; st < npre; st++) issue_stage<D, WK, 8>(stage_slot(st), kbeg + st * WK * 32, sl);
+  for (int st = 0; st < npre; st++) issue_stage<F, D, WK, 8>(stage_slot(st), kbeg + st * WK * TK, sl);
 
-  const LaneOffsets<D> lo = lane_offsets<D>(lane);
+  const auto lo = [&] {
+    if constexpr (F8) return lane_offsets8(lane);
+    else return lane_offsets<D>(lane);
+  }();
+
   const int wave_qi_min = div_rcp(row0 + 32 * rg, plan.rcp_g);
   const int wave_qi_max = div_rcp(row0 + 32 * rg + 31, plan.rcp_g);
   const float c2 = a.scale_log2;
@@ -597,28 +884,41 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
     for (int i = 0; i < 16; i++) acc.o[mb][i] = 0.f;
   acc.mlog = -1e30f;  // log2-domain reference max; finite so rescales never form inf-inf
   acc.lsum = 0.f;
-  acc.thr = (acc.mlog + kRescaleThreshold) / c2;
+  acc.thr = (acc.mlog + (F::kBias + F::kThreshold)) / c2;
 
-  // Chunk k of this wave is tile t = k*WK + kg of the unit (keys kbeg + 32t ..).
+  // Chunk k of this wave is tile t = k*WK + kg of the unit (keys kbeg + TK*t ..).
   // It holds visible keys iff k < nok; its scores need masking iff k >= kmask
   // (ragged end of the unit, or for the commit a tile reaching past the
   // diagonal of the wave's first query).
-  const int tvis = klimit > kbeg ? (klimit - kbeg + 31) / 32 : 0;
+  const int tvis = klimit > kbeg ? (klimit - kbeg + TK - 1) / TK : 0;
   const int nok = tvis > kg ? (tvis - kg + WK - 1) / WK : 0;
-  int tmask = (kstop - kbeg) / 32;
+  int tmask = (kstop - kbeg) / TK;
   if (CAUSAL) {
-    const int x = wave_qi_min + L - 31 - kbeg;
-    tmask = min(tmask, x >= 0 ? x / 32 + 1 : 0);
+    const int x = wave_qi_min + L - (TK - 1) - kbeg;
+    tmask = min(tmask, x >= 0 ? x / TK + 1 : 0);
   }
   const int kmask = tmask > kg ? (tmask - kg + WK - 1) / WK : 0;
 
-  auto chunk_key = [&](int k) { return kbeg + (k * WK + kg) * 32; };
+  auto chunk_key = [&](int k) { return kbeg + (k * WK + kg) * TK; };
   // per-lane operand addresses in stage 0 of this wave's key group
-  uint32_t kaddr[KS], vaddr[MB];
+  using Ops = typename std::conditional<F8, Ops8, Ops16<D>>::type;
+  using KAddr = typename std::conditional<F8, uint32_t[2][2], uint32_t[KS]>::type;
+  KAddr kaddr;
+  uint32_t vaddr[MB];
+  Ops op;
+  if constexpr (F8) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ks++) kaddr[ks] = lring + kg * TILEB + lo.k[ks];
+    for (int ks = 0; ks < 2; ks++)
 #pragma unroll
-  for (int mb = 0; mb < MB; mb++) vaddr[mb] = lring + kVRegion + kg * TILEB + lo.v[mb];
+      for (int part = 0; part < 2; part++) kaddr[ks][part] = lring + kg * TILEB + lo.k[ks][part];
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) vaddr[mb] = lring + kVRegion + kg * TILEB + lo.v[mb];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) kaddr[ks] = lring + kg * TILEB + lo.k[ks];
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) vaddr[mb] = lring + kVRegion + kg * TILEB + lo.v[mb];
+  }
 
   // ---- prologue.  Barrier A: the queries and stage 0 (the wave's own loads of
   //      them are its oldest npre*GPW .. ones) are in LDS; the wave reads its query
@@ -628,28 +928,27 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(GPW) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  bf16x8 qr[KS];    // B operands of S^T = K Q^T: lane (n, h), k-step ks holds
-                    // q[row][D/2*h + 8*ks .. +8] (the permutation of head_dim the K
-                    // operands use too)
+  if constexpr (F8) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ks++)
-    qr[ks] = *(const LDS_AS bf16x8*)(uintptr_t)(q_lds(32 * rg) + lo.k[ks]);
-  f32x16 s_nx;      // scores of the chunk the next softmax works on
-  bf16x8 kop[KS];   // K operands for the next score MFMAs
-  bf16x8 vop[MB][2];// V^T operands for the next value MFMAs
-  bf16x8 pb[2];     // packed exponentials for the next value MFMAs
+    for (int ks = 0; ks < 2; ks++)
+      op.q[ks] = lds_read_2x16(q_lds(32 * rg) + lo.q[ks][0], q_lds(32 * rg) + lo.q[ks][1]);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+      op.q[ks] = *(const LDS_AS bf16x8*)(uintptr_t)(q_lds(32 * rg) + lo.k[ks]);
+  }
   if (0 < nok) {
-    load_k_operands<D>(kaddr, 0, kop);
-    scores<D>(kop, qr, s_nx);
-    load_v_operands<D>(vaddr, 0, vop);
+    load_k_operands(kaddr, 0, op);
+    scores(op);
+    load_v_operands(vaddr, 0, op);
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   for (int st = 2; st < min(NSLOT, nstages); st++)
-    issue_stage<D, WK, 8>(stage_slot(st), kbeg + st * WK * 32, sl);
-  if (1 < nok) load_k_operands<D>(kaddr, SSTR % (NSLOT * SSTR), kop);
+    issue_stage<F, D, WK, 8>(stage_slot(st), kbeg + st * WK * TK, sl);
+  if (1 < nok) load_k_operands(kaddr, SSTR % (NSLOT * SSTR), op);
   if (0 < nok) {
-    prepare_scores<MB, CAUSAL>(s_nx, 0 >= kmask, chunk_key(0), kstop, L, qi, h, c2, acc);
-    numerators<MB>(s_nx, c2, acc, pb);
+    prepare_scores<MB, CAUSAL>(op, 0 >= kmask, chunk_key(0), kstop, L, qi, h, c2, acc);
+    numerators<MB>(op, c2, acc);
   }
 
   auto barrier_e = [&](bool after_x0) {  // barrier E: stage 2 complete
@@ -682,16 +981,16 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
       // chunk k+1 run (the issue slots of an MFMA phase are otherwise idle)
       __builtin_amdgcn_sched_barrier(0);
       if (grp == 1 && k == 0) barrier_e(false);
-      if (k + NSLOT < nstages) issue_stage<D, WK, 8>(stage_slot(j), kbeg + (k + NSLOT) * WK * 32, sl);
+      if (k + NSLOT < nstages) issue_stage<F, D, WK, 8>(stage_slot(j), kbeg + (k + NSLOT) * WK * TK, sl);
       __builtin_amdgcn_s_setprio(1);
-      if (k < nok) values<MB>(vop, pb, acc);
+      if (k < nok) values<MB>(op, acc);
       if (k + 1 < nok) {
-        scores<D>(kop, qr, s_nx);
-        load_v_operands<D>(vaddr, off1, vop);
+        scores(op);
+        load_v_operands(vaddr, off1, op);
 #pragma unroll
-        for (int i = 0; i < KS; i++) {
+        for (int i = 0; i < NSM; i++) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one score MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 4 * MB / KS, 0);  // two V reads
+          __builtin_amdgcn_sched_group_barrier(0x100, NVR / NSM, 0);    // its share of V reads
         }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -702,9 +1001,9 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
       // Y(k): K operands of chunk k+2 (for X(k+1); a chunk past the wave's last is
       // read too and not used), softmax of chunk k+1 (vector ALU)
       if (k + 1 < nok) {
-        load_k_operands<D>(kaddr, off2, kop);
-        prepare_scores<MB, CAUSAL>(s_nx, k + 1 >= kmask, chunk_key(k + 1), kstop, L, qi, h, c2, acc);
-        numerators<MB>(s_nx, c2, acc, pb);
+        load_k_operands(kaddr, off2, op);
+        prepare_scores<MB, CAUSAL>(op, k + 1 >= kmask, chunk_key(k + 1), kstop, L, qi, h, c2, acc);
+        numerators<MB>(op, c2, acc);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (grp == 0) ring_barrier(k);
@@ -761,9 +1060,13 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
   //      output (single split) or as this split's partial rows.  They go out
   //      through a per-wave LDS staging area, 64 columns of head_dim at a time, so
   //      that every store is a whole 128-byte row segment (the accumulator layout
-  //      puts one query row in each lane).
+  //      puts one query row in each lane).  fp8 rows also take the value scale.
   const float lt = partner_sum(acc.lsum);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  float inv;
+  if constexpr (F8)
+    inv = lt > 0.f ? a.out_scale / lt : 0.f;
+  else
+    inv = lt > 0.f ? 1.f / lt : 0.f;
   const bool direct = sp.n_splits == 1;
   constexpr int SROWB = 64 * 2 + 16;  // bytes per staged row (padding spreads banks)
   // staging past the merge buffer, so that no wave's staging overwrites state
@@ -800,6 +1103,16 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan
   }
   if (!direct && h == 0)
     *(float2*)(a.part_ml + ((int64_t)U * R + (prow - row0)) * 2) = make_float2(acc.mlog, lt);
+}
+
+template <int D, bool CAUSAL, int WM, int WK, int NSLOT>
+__global__ __launch_bounds__(512, 2) void attn_bf16_kernel(AttnArgs a, Plan plan) {
+  attn_body<FmtBf16, D, CAUSAL, WM, WK, NSLOT>(a, plan);
+}
+
+template <int D, bool CAUSAL, int WM, int WK, int NSLOT>
+__global__ __launch_bounds__(512, 2) void attn_fp8_kernel(AttnArgs a, Plan plan) {
+  attn_body<FmtFp8, D, CAUSAL, WM, WK, NSLOT>(a, plan);
 }
 
 // ---------------------------------------------------------------------------
@@ -924,8 +1237,8 @@ void attn_rows_kernel(AttnArgs a, Plan plan) {
     for (int ks = 0; ks < KS; ks++) qr[rb][ks] = *(const bf16x8*)(qp + 8 * ks);
   }
 
-  StageLoads<D, 1, NW> sl;
-  stage_loads_init<D, 1, NW>(sl, (const char*)(kc + ((int64_t)u.b * cap * Hkv + u.g) * D),
+  StageLoads<FmtBf16, D, 1, NW> sl;
+  stage_loads_init<FmtBf16, D, 1, NW>(sl, (const char*)(kc + ((int64_t)u.b * cap * Hkv + u.g) * D),
                              (const char*)(vc + ((int64_t)u.b * cap * Hkv + u.g) * D),
                              (const char*)(kn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
                              (const char*)(vn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
@@ -967,7 +1280,7 @@ void attn_rows_kernel(AttnArgs a, Plan plan) {
   //      complete, so before B(j-3) each wave waits for its own loads of it.
   const int npre = min(NSLOT, nstages);
   for (int st = 0; st < npre; st++)
-    issue_stage<D, 1, NW>(lring + (uint32_t)(st & (NSLOT - 1)) * SSTR, kbeg + st * 32, sl);
+    issue_stage<FmtBf16, D, 1, NW>(lring + (uint32_t)(st & (NSLOT - 1)) * SSTR, kbeg + st * 32, sl);
   if (nstages >= NSLOT)
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSLOT - 3) * GPW) : "memory");
   else
@@ -1028,7 +1341,7 @@ void attn_rows_kernel(AttnArgs a, Plan plan) {
       else
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       if (k + NSLOT < nstages)
-        issue_stage<D, 1, NW>(lring + (uint32_t)j * SSTR, kbeg + (k + NSLOT) * 32, sl);
+        issue_stage<FmtBf16, D, 1, NW>(lring + (uint32_t)j * SSTR, kbeg + (k + NSLOT) * 32, sl);
     }
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -1092,11 +1405,22 @@ int launch_rows(const AttnArgs& a, const Plan& p, hipStream_t st) {
 template <bool CAUSAL>
 int launch_d128(const AttnArgs& a, const Plan& p, hipStream_t st) {
   if (p.variant == kVariantR256) return launch_one<128, CAUSAL, 8, 1, 8>(a, p, st);
-  if (p.variant == kVariantF8) return launch_rows<128, CAUSAL, 1, 8>(a, p, st);
+  if (p.variant == kVariantFree) return launch_rows<128, CAUSAL, 1, 8>(a, p, st);
   return launch_one<128, CAUSAL, 4, 2, 4>(a, p, st);  // kVariantR128
 }
 
+template <bool CAUSAL>
+int launch_fp8(const AttnArgs& a, const Plan& p, hipStream_t st) {
+  hipLaunchKernelGGL((attn_fp8_kernel<128, CAUSAL, 4, 2, 4>), dim3(p.n_units), dim3(512), 0, st, a, p);
+  return (int)hipGetLastError();
+}
+
 }  // namespace
+
+int launch_attn_fp8(const AttnArgs& a, const Plan& p, bool causal, void* stream) {
+  if (p.n_units == 0) return 0;
+  return causal ? launch_fp8<true>(a, p, (hipStream_t)stream) : launch_fp8<false>(a, p, (hipStream_t)stream);
+}
 
 int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream) {
   hipStream_t st = (hipStream_t)stream;

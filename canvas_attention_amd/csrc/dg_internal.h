@@ -37,9 +37,9 @@ struct SeqPlan {
 inline uint32_t rcp_u32(uint32_t d) { return d <= 1 ? 0u : (uint32_t)((1ull << 32) / d + 1); }
 
 // bf16 kernel shapes.  R256 and R128: eight waves of 32 packed rows (row groups x
-// key groups, waves paired on a SIMD in ping-pong); F8: eight free-running waves
-// of 32 rows (256 rows per unit).
-enum { kVariantR256 = 0, kVariantR128 = 1, kVariantF8 = 2, kNumVariants = 3 };
+// key groups, waves paired on a SIMD in ping-pong); Free: eight free-running waves
+// of 32 rows (256 rows per unit).  The fp8 kernel has the R128 shape.
+enum { kVariantR256 = 0, kVariantR128 = 1, kVariantFree = 2, kNumVariants = 3 };
 constexpr int kDefaultVariant = kVariantR128;
 inline int variant_rows(int v) { return v == kVariantR128 ? 128 : 256; }
 
@@ -72,12 +72,14 @@ struct AttnArgs {
   int64_t cap;
   int32_t n_heads_q;
   int32_t n_heads_kv;
-  float scale_log2;     // softmax scale * log2(e)
+  float scale_log2;     // softmax scale * log2(e) (fp8: times the q and k scales)
+  float out_scale;      // fp8: the v scale, applied with the normalisation (else 1)
 };
 
 // Host-side launchers (defined next to their kernels).  Each returns the HIP
 // error of the launch.
 int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream);
+int launch_attn_fp8(const AttnArgs& a, const Plan& p, bool causal, void* stream);
 int launch_attn_f32(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream);
 int launch_merge(const AttnArgs& a, const Plan& p, int head_dim, bool bf16_out, void* stream);
 

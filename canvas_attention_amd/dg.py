@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # compiled with different tuning flags); the default is the in-tree build.
 LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(_HERE, "libdg.so")
 
-DG_BF16, DG_F32 = 0, 1
+DG_BF16, DG_F32, DG_FP8 = 0, 1, 2
 N_CANVAS = 256
 STATUS = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_DTYPE",
           -4: "DG_ERR_CAPACITY", -5: "DG_ERR_WORKSPACE", -6: "DG_ERR_HIP", -7: "DG_ERR_ALIGN"}
@@ -32,7 +32,8 @@ class DgShape(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("n_canvas", ctypes.c_int32), ("n_heads_q", ctypes.c_int32),
                 ("n_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("q_scale", ctypes.c_float),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class DgKv(ctypes.Structure):
@@ -84,17 +85,26 @@ def _check(fn, status):
         raise DgError(fn, status, lib.dg_last_error().decode())
 
 
-def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
+def _dtype_code(dtype) -> int:
+    if dtype == torch.bfloat16:
         return DG_BF16
-    if t.dtype == torch.float32:
+    if dtype == torch.float32:
         return DG_F32
-    raise TypeError(f"unsupported dtype {t.dtype}; bfloat16 or float32")
+    if dtype == torch.float8_e4m3fn:
+        return DG_FP8
+    raise TypeError(f"unsupported dtype {dtype}; bfloat16, float32 or float8_e4m3fn")
 
 
-def _shape(q: torch.Tensor, hkv: int, scale) -> DgShape:
+def out_dtype(dtype):
+    """Output element type for inputs of `dtype` (fp8 inputs give bf16 rows)."""
+    return torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype
+
+
+def _shape(q: torch.Tensor, hkv: int, scale, tensor_scales=None) -> DgShape:
     B, Nc, Hq, D = q.shape
-    return DgShape(_dtype_code(q), B, Nc, Hq, hkv, D, float(scale) if scale else 0.0)
+    qs, ks, vs = tensor_scales if tensor_scales is not None else (0.0, 0.0, 0.0)
+    return DgShape(_dtype_code(q.dtype), B, Nc, Hq, hkv, D, float(scale) if scale else 0.0,
+                   float(qs), float(ks), float(vs))
 
 
 def _ptr(t):
@@ -128,8 +138,7 @@ def _prefix(prefix_len, batch):
 def workspace_bytes(batch, n_heads_q, n_heads_kv, head_dim, max_prefix_len,
                     dtype=torch.bfloat16) -> int:
     """Bytes of workspace any call of this shape needs (see dg_workspace_bytes)."""
-    code = DG_BF16 if dtype == torch.bfloat16 else DG_F32
-    shape = DgShape(code, batch, N_CANVAS, n_heads_q, n_heads_kv, head_dim, 0.0)
+    shape = DgShape(_dtype_code(dtype), batch, N_CANVAS, n_heads_q, n_heads_kv, head_dim, 0.0)
     n = lib.dg_workspace_bytes(ctypes.byref(shape), int(max_prefix_len))
     if n == 0:
         # zero is also the answer for a valid shape that needs no partials
@@ -144,8 +153,10 @@ def alloc_workspace(q: torch.Tensor, n_heads_kv: int, max_prefix_len: int) -> to
 
 
 def canvas_attn(q, k_cache, v_cache, prefix_len, k_canvas, v_canvas, out=None, workspace=None,
-                scale=None, stream=None):
-    """dg_canvas_attn: q [B,256,Hq,D]; caches [B,cap,Hkv,D]; canvas K/V [B,256,Hkv,D]."""
+                scale=None, stream=None, tensor_scales=None):
+    """dg_canvas_attn: q [B,256,Hq,D]; caches [B,cap,Hkv,D]; canvas K/V [B,256,Hkv,D].
+    float8_e4m3fn inputs take tensor_scales = (q_scale, k_scale, v_scale) and give
+    a bfloat16 output."""
     dt = q.dtype
     _need(q, "q", dt, 4)
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_canvas", k_canvas),
@@ -153,11 +164,11 @@ def canvas_attn(q, k_cache, v_cache, prefix_len, k_canvas, v_canvas, out=None, w
         _need(t, name, dt, 4)
     hkv = k_cache.shape[2]
     if out is None:
-        out = torch.empty_like(q)
-    _need(out, "out", dt, 4)
+        out = torch.empty(q.shape, dtype=out_dtype(dt), device=q.device)
+    _need(out, "out", out_dtype(dt), 4)
     if workspace is None:
         workspace = alloc_workspace(q, hkv, max(int(x) for x in prefix_len))
-    shape = _shape(q, hkv, scale)
+    shape = _shape(q, hkv, scale, tensor_scales)
     cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])
     canv = DgKv(k_canvas.data_ptr(), v_canvas.data_ptr(), k_canvas.shape[1])
     st = lib.dg_canvas_attn(ctypes.byref(shape), _ptr(q), ctypes.byref(cache),
@@ -169,7 +180,7 @@ def canvas_attn(q, k_cache, v_cache, prefix_len, k_canvas, v_canvas, out=None, w
 
 
 def commit_block(q_blk, k_blk, v_blk, k_cache, v_cache, prefix_len, out=None, workspace=None,
-                 scale=None, stream=None):
+                 scale=None, stream=None, tensor_scales=None):
     """dg_commit_block: causal block attention, then block K/V appended to the cache."""
     dt = q_blk.dtype
     _need(q_blk, "q_blk", dt, 4)
@@ -178,11 +189,11 @@ def commit_block(q_blk, k_blk, v_blk, k_cache, v_cache, prefix_len, out=None, wo
         _need(t, name, dt, 4)
     hkv = k_cache.shape[2]
     if out is None:
-        out = torch.empty_like(q_blk)
-    _need(out, "out", dt, 4)
+        out = torch.empty(q_blk.shape, dtype=out_dtype(dt), device=q_blk.device)
+    _need(out, "out", out_dtype(dt), 4)
     if workspace is None:
         workspace = alloc_workspace(q_blk, hkv, max(int(x) for x in prefix_len))
-    shape = _shape(q_blk, hkv, scale)
+    shape = _shape(q_blk, hkv, scale, tensor_scales)
     blk = DgKv(k_blk.data_ptr(), v_blk.data_ptr(), k_blk.shape[1])
     cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])
     st = lib.dg_commit_block(ctypes.byref(shape), _ptr(q_blk), ctypes.byref(blk),
@@ -194,7 +205,7 @@ def commit_block(q_blk, k_blk, v_blk, k_cache, v_cache, prefix_len, out=None, wo
 
 
 def canvas_step_loop(q_steps, k_steps, v_steps, k_cache, v_cache, prefix_len, out=None,
-                     workspace=None, scale=None, stream=None):
+                     workspace=None, scale=None, stream=None, tensor_scales=None):
     """dg_canvas_step_loop over N steps: q_steps [N,B,256,Hq,D], k/v_steps [N,B,256,Hkv,D]."""
     dt = q_steps.dtype
     _need(q_steps, "q_steps", dt, 5)
@@ -205,12 +216,12 @@ def canvas_step_loop(q_steps, k_steps, v_steps, k_cache, v_cache, prefix_len, ou
     n = q_steps.shape[0]
     hkv = k_cache.shape[2]
     if out is None:
-        out = torch.empty_like(q_steps)
-    _need(out, "out", dt, 5)
+        out = torch.empty(q_steps.shape, dtype=out_dtype(dt), device=q_steps.device)
+    _need(out, "out", out_dtype(dt), 5)
     q0 = q_steps[0]
     if workspace is None:
         workspace = alloc_workspace(q0, hkv, max(int(x) for x in prefix_len))
-    shape = _shape(q0, hkv, scale)
+    shape = _shape(q0, hkv, scale, tensor_scales)
     canv = DgKv(k_steps.data_ptr(), v_steps.data_ptr(), k_steps.shape[2])
     cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])
     st = lib.dg_canvas_step_loop(ctypes.byref(shape), n, _ptr(q_steps), q_steps[0].numel(),

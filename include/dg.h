@@ -17,10 +17,18 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Element type: DG_BF16 (bf16 storage, fp32 accumulation, bf16 output rounded
- * to nearest-even) or DG_F32 (fp32 storage and arithmetic throughout).
+ * to nearest-even), DG_F32 (fp32 storage and arithmetic throughout) or DG_FP8
+ * (queries, keys and values stored as OCP e4m3 -- 1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, subnormals, largest finite value 448, bytes 0x7f and
+ * 0xff NaN, no infinities -- each tensor with a per-tensor scale, so that the
+ * value an element stands for is scale * e4m3 value; fp32 accumulation, the
+ * softmax weights rounded to e4m3 for the value product, bf16 output rounded to
+ * nearest-even; head_dim 128 only).  The fp8 element type is the deployment
+ * precision of the report's throughput figures (section "The numbers, honestly":
+ * H100, FP8).
  *
  * Layouts (all row-major, element strides implied by the shape):
- *   queries q, q_blk, out ......... [B][Nc][Hq][D]
+ *   queries q, q_blk, out ......... [B][Nc][Hq][D]   (out is bf16 for DG_FP8)
  *   canvas / block K, V ........... [B][Nc][Hkv][D]     (dg_kv.capacity = Nc)
  *   cache K, V .................... [B][capacity][Hkv][D]
  * Query head h reads kv head h / (Hq / Hkv) (grouped-query attention with
@@ -62,20 +70,26 @@ enum {
   DG_ERR_ALIGN = -7      /* a device pointer is not 16-byte aligned             */
 };
 
-enum { DG_BF16 = 0, DG_F32 = 1 };
+enum { DG_BF16 = 0, DG_F32 = 1, DG_FP8 = 2 };
 
 /* Limits checked by every entry point. */
 #define DG_N_CANVAS 256  /* canvas / block length: fixed at 256 positions      */
 #define DG_MAX_BATCH 64  /* sequences per call                                  */
 
 typedef struct {
-  int32_t dtype;      /* DG_BF16 or DG_F32                                       */
+  int32_t dtype;      /* DG_BF16, DG_F32 or DG_FP8                               */
   int32_t batch;      /* B, 1..DG_MAX_BATCH                                      */
   int32_t n_canvas;   /* Nc, must equal DG_N_CANVAS                              */
   int32_t n_heads_q;  /* Hq >= 1, a multiple of n_heads_kv                       */
   int32_t n_heads_kv; /* Hkv >= 1                                               */
-  int32_t head_dim;   /* D: 64 or 128                                           */
+  int32_t head_dim;   /* D: 64 or 128 (DG_FP8: 128)                             */
   float scale;        /* softmax scale; <= 0 selects 1/sqrt(D)                   */
+  /* DG_FP8 only (ignored otherwise): the per-tensor scales of q (canvas or block
+   * queries), of K (cache and canvas or block keys alike: the commit appends block
+   * rows to the cache bit for bit) and of V; <= 0 selects 1.  Must be finite.    */
+  float q_scale;
+  float k_scale;
+  float v_scale;
 } dg_shape;
 
 /* A pair of K and V buffers, each [B][capacity][Hkv][D]. */
@@ -97,6 +111,7 @@ size_t dg_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len);
  * Canvas denoising step (bidirectional decoder of the mechanism section).
  * For every sequence b, query head h and canvas row i:
  *   out[b,i,h,:] = softmax_j(scale * <q[b,i,h,:], k_j>) v_j
+ * (with DG_FP8, q, k_j and v_j are the scaled e4m3 values and out is bf16)
  * over j in { cache rows 0..prefix_len[b]-1 } U { canvas rows 0..Nc-1 } of kv
  * head h / (Hq/Hkv); no mask.  The cache is only read.
  *   q          [B][Nc][Hq][D] device
@@ -135,8 +150,9 @@ dg_status dg_commit_block(const dg_shape* shape, const void* q_blk, const dg_kv*
  * a block), enqueued in order on `stream`.  Step s reads
  *   q + s*q_step_stride, kv_canvas->k + s*kv_step_stride,
  *   kv_canvas->v + s*kv_step_stride
- * and writes out + s*out_step_stride (all strides in elements, each step laid
- * out as for dg_canvas_attn).  The result is bit for bit that of n_steps
+ * and writes out + s*out_step_stride (all strides in elements of the tensor
+ * they step: input elements for q and K/V, output elements for out; each step
+ * laid out as for dg_canvas_attn).  The result is bit for bit that of n_steps
  * separate dg_canvas_attn calls: in the model each step's queries depend on
  * the previous step's output, so steps are never fused; the loop plans once
  * and only removes per-call host work.  n_steps >= 0; the workspace is reused

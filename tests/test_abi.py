@@ -75,6 +75,9 @@ def call_commit(dg, sh, cache=None, prefix=(0,), ws_bytes=1 << 40):
     (dict(head_dim=96), -2),
     (dict(n_heads_kv=0), -2),
     (dict(scale=float("nan")), -2),
+    (dict(dtype=2, head_dim=64), -2),
+    (dict(dtype=2, q_scale=float("inf")), -2),
+    (dict(dtype=2, v_scale=float("nan")), -2),
 ])
 def test_shape_errors(dg, kw, code):
     st = call_canvas(dg, shape(dg, **kw), prefix=(0,) * max(1, kw.get("batch", 1) or 1))
@@ -124,6 +127,18 @@ def test_step_loop_errors(dg):
     assert st == -7
 
 
+def test_fp8_step_strides(dg):
+    # fp8 steps q and K/V in 1-byte elements and out in 2-byte (bf16) elements
+    sh = shape(dg, dtype=2)
+    cache = dg.DgKv(FAKE, FAKE, 4096)
+    canv = dg.DgKv(FAKE, FAKE, 256)
+    pl = (ctypes.c_int32 * 1)(0)
+    for qs, kvs, os_ in ((8, 16, 8), (16, 24, 8), (16, 16, 4)):
+        st = dg.lib.dg_canvas_step_loop(ctypes.byref(sh), 2, FAKE, qs, ctypes.byref(canv), kvs,
+                                        ctypes.byref(cache), pl, FAKE, os_, FAKE, 1 << 40, None)
+        assert st == -7, (qs, kvs, os_, st)
+
+
 def test_workspace_bytes(dg):
     assert dg.lib.dg_workspace_bytes(ctypes.byref(shape(dg, head_dim=96)), 1000) == 0
     assert dg.lib.dg_workspace_bytes(ctypes.byref(shape(dg)), -1) == 0
@@ -131,6 +146,10 @@ def test_workspace_bytes(dg):
     assert n > 0 and n % 4 == 0
     n32 = dg.lib.dg_workspace_bytes(ctypes.byref(shape(dg, dtype=1, head_dim=64)), 64)
     assert n32 > 0
+    # fp8 partial rows are bf16, as for the bf16 path
+    n8 = dg.lib.dg_workspace_bytes(ctypes.byref(shape(dg, dtype=2)), 8192)
+    assert n8 == n
+    assert dg.lib.dg_workspace_bytes(ctypes.byref(shape(dg, dtype=2, head_dim=64)), 64) == 0
 
 
 def test_status_strings(dg):
