@@ -55,9 +55,15 @@ static double e4m3_value(uint8_t c) {
   return sign ? -mag : mag;
 }
 
+/* e4m3_value of every byte, filled before the row loops read it. */
+static double e4m3_table[256];
+
+static void fill_e4m3_table(void) {
+  for (int c = 0; c < 256; c++) e4m3_table[c] = e4m3_value((uint8_t)c);
+}
+
 /* Exact widening of one stored element to double. */
-static double ld(const void* p, int dtype, int64_t i) {
-  if (dtype == DGO_FP8) return e4m3_value(((const uint8_t*)p)[i]);
+static inline __attribute__((always_inline)) double ld(const void* p, int dtype, int64_t i) {
   if (dtype == DGO_BF16) {
     uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
     float f;
@@ -65,6 +71,7 @@ static double ld(const void* p, int dtype, int64_t i) {
     return (double)f;
   }
   if (dtype == DGO_F32) return (double)((const float*)p)[i];
+  if (dtype == DGO_FP8) return e4m3_table[((const uint8_t*)p)[i]];
   return ((const double*)p)[i];
 }
 
@@ -95,6 +102,10 @@ static void attend_row(const dgo_args* a, int b, int i, int h, double* scores, d
   const int64_t n_vis = a->causal ? (int64_t)i + 1 : (int64_t)a->Nc;
   const int64_t n_keys = L + n_vis;
   const int64_t q_off = (((int64_t)b * a->Nc + i) * a->Hq + h) * D;
+  /* The tensor scales multiply each stored element; they are applied to the
+   * dot product (q and k scales, with the softmax scale) and to the weighted sum
+   * of values (v scale), which is the same in exact arithmetic. */
+  const double qk_scale = a->qs * a->ks * a->scale;
 
   /* pass 1: scores and their maximum */
   double m = -INFINITY;
@@ -109,9 +120,8 @@ static void attend_row(const dgo_args* a, int b, int i, int h, double* scores, d
       k_off = (((int64_t)b * a->Nc + (j - L)) * a->Hkv + g) * D;
     }
     double s = 0.0;
-    for (int d = 0; d < D; d++)
-      s += (a->qs * ld(a->q, a->dtype, q_off + d)) * (a->ks * ld(kp, a->dtype, k_off + d));
-    s *= a->scale;
+    for (int d = 0; d < D; d++) s += ld(a->q, a->dtype, q_off + d) * ld(kp, a->dtype, k_off + d);
+    s *= qk_scale;
     scores[j] = s;
     if (s > m) m = s;
   }
@@ -130,9 +140,9 @@ static void attend_row(const dgo_args* a, int b, int i, int h, double* scores, d
       vp = a->v_new;
       v_off = (((int64_t)b * a->Nc + (j - L)) * a->Hkv + g) * D;
     }
-    for (int d = 0; d < D; d++) out[d] += p * (a->vs * ld(vp, a->dtype, v_off + d));
+    for (int d = 0; d < D; d++) out[d] += p * ld(vp, a->dtype, v_off + d);
   }
-  for (int d = 0; d < D; d++) out[d] /= l;
+  for (int d = 0; d < D; d++) out[d] = a->vs * out[d] / l;
 }
 
 static int check(const dgo_args* a) {
@@ -153,6 +163,7 @@ static int check(const dgo_args* a) {
 static int run(const dgo_args* a, int n_rows, const int32_t* rows, double* out) {
   int rc = check(a);
   if (rc) return rc;
+  if (a->dtype == DGO_FP8) fill_e4m3_table();
   int64_t max_keys = 0;
   for (int b = 0; b < a->B; b++)
     if (a->prefix_len[b] + a->Nc > max_keys) max_keys = a->prefix_len[b] + a->Nc;
