@@ -3,16 +3,18 @@
 One step = one block cycle of the L=8192 workload: 12 canvas denoising steps
 (dg_canvas_step_loop, fresh seeded Q/K/V per step, fixed cache) followed by the
 causal commit of the block with its cache append (dg_commit_block), batch 1,
-Hq=16, Hkv=8, head_dim=128, bf16 storage with fp32 accumulation.
+Hq=16, Hkv=8, head_dim=128, bf16 storage with fp32 accumulation (--dtype fp8:
+OCP e4m3 storage with tensor scales 1, fp32 accumulation, bf16 output).
 
 Prints one JSON line.  value = algorithmic TFLOP/s of the whole cycle
 (canvas step 4*B*Hq*256*(L+256)*D, commit 4*B*Hq*D*(256*L + 256*257/2), exp
 and max not counted).  The roofline object is for the dominant kernel (the
 split-key canvas attention kernel), timed with HIP events that the library
 records on its launch stream.  cpu_baseline times the CPU fp64 oracle on a
-bounded sample of the same workload.
+bounded sample of the same workload.  The default (bf16) line also carries the
+fp8 canvas step's kernel time and its fraction of the fp8 MFMA peak.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--dtype fp8]
 """
 from __future__ import annotations
 
@@ -29,15 +31,26 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "canvas-step attn TFLOP/s + canvas positions/s at L=8k, bs=1; % MFMA peak"
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA
+PEAK_BF16_TFLOPS = PEAK_TFLOPS["bf16"]
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+ELEM_BYTES = {"bf16": 2, "fp8": 1}
+
+# the canvas attention kernel of each format, as rocprofv3 names it, and the
+# profile files of its counter summaries
+ATTN_KERNELS = {"bf16": "attn_bf16_kernel<128, false", "fp8": "attn_fp8_kernel<128, false"}
+PROFILE_TAG = {"bf16": "canvas_attn_l8k", "fp8": "canvas_attn_fp8_l8k"}
+MOPS_COUNTER = {"bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "fp8": "SQ_INSTS_VALU_MFMA_MOPS_F8"}
+
+
+def traffic_file(dtype):
+    return os.path.join(ROOT, "profiles", PROFILE_TAG[dtype] + "_traffic.txt")
 
 
 # HBM traffic of the dominant kernel comes from rocprofv3 counter runs
 # (FETCH_SIZE and WRITE_SIZE per dispatch, calibrated against a plain copy of
-# known size) recorded in this file together with a hash of the kernel source;
-# it is reported only while the source still matches.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "canvas_attn_l8k_traffic.txt")
+# known size) recorded in a profile file together with a hash of the kernel
+# source; it is reported only while the source still matches.
 KERNEL_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
                   for f in ("dg_attn_mfma.hip", "dg_internal.h")]
 
@@ -50,13 +63,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(dtype="bf16"):
     """Bytes per launch of the canvas attention kernel from the counter file, or
     None when the file is absent or was taken on another version of the kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(dtype)
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -98,10 +112,9 @@ def _counter_per_dispatch(folder, counter, name_part):
     return sum(vals.values()) / len(vals), len(vals)
 
 
-ATTN_KERNEL = "attn_bf16_kernel<128, false"
-
-
-def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib):
+def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, dtype="bf16"):
+    ATTN_KERNEL = ATTN_KERNELS[dtype]
+    flag = "" if dtype == "bf16" else f" --dtype {dtype}"
     copy_bytes = int(copy_mib) * (1 << 20)
     f_kib, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", ATTN_KERNEL)
     w_kib, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", ATTN_KERNEL)
@@ -112,13 +125,14 @@ def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib):
     fetch = f_kib * 1024.0 * f_scale
     write = w_kib * 1024.0 * w_scale
     lines = [
-        "# HBM traffic of the canvas attention kernel (canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)",
+        f"# HBM traffic of the canvas attention kernel ({dtype}; canvas step, L=8192, B=1, Hq=16, "
+        "Hkv=8, D=128)",
         "# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of",
-        "#   python3 bench.py --steps 2 --warmup 1 --profile-steps",
+        f"#   python3 bench.py --steps 2 --warmup 1 --profile-steps{flag}",
         "# calibrated with the same counters on a plain device-to-device copy of known size",
         f"#   python3 bench.py --copy-probe {copy_mib}",
         "# (each scale = copy bytes / counter bytes of that copy); written by",
-        "#   python3 bench.py --summarize-counters FETCH WRITE COPY_FETCH COPY_WRITE MIB",
+        f"#   python3 bench.py --summarize-counters FETCH WRITE COPY_FETCH COPY_WRITE MIB{flag}",
         f"kernel: {ATTN_KERNEL}...>",
         f"kernel_source_hash: {kernel_source_hash()}",
         f"dispatches_fetch: {nf}",
@@ -134,19 +148,22 @@ def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib):
         f"write_bytes_per_launch: {write:.0f}",
         f"traffic_bytes_per_launch: {fetch + write:.0f}",
     ]
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as fh:
+    os.makedirs(os.path.dirname(traffic_file(dtype)), exist_ok=True)
+    with open(traffic_file(dtype), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def summarize_mfma(pass1_dir, pass2_dir, trace_txt):
+def summarize_mfma(pass1_dir, pass2_dir, trace_txt, dtype="bf16"):
     """MFMA work of the canvas attention kernel from two rocprofv3 --pmc runs of
     `bench.py --steps 2 --warmup 1 --profile-steps` (SQ_VALU_MFMA_BUSY_CYCLES,
-    SQ_INSTS_MFMA; SQ_INSTS_VALU_MFMA_MOPS_BF16), set against the kernel's average
-    duration from the kernel-trace summary.  Writes profiles/canvas_attn_l8k_mfma.txt."""
+    SQ_INSTS_MFMA; SQ_INSTS_VALU_MFMA_MOPS_BF16 or _F8), set against the kernel's
+    average duration from the kernel-trace summary.  Writes
+    profiles/<tag>_mfma.txt."""
     import csv
     import collections
+    ATTN_KERNEL = ATTN_KERNELS[dtype]
+    flag = "" if dtype == "bf16" else f" --dtype {dtype}"
 
     def per_dispatch(d):
         vals = collections.defaultdict(lambda: collections.defaultdict(float))
@@ -161,21 +178,23 @@ def summarize_mfma(pass1_dir, pass2_dir, trace_txt):
         if ATTN_KERNEL in line:
             avg_us = float(line.split()[1])
     busy = c["SQ_VALU_MFMA_BUSY_CYCLES"][0] / 1024.0  # per SIMD (256 CUs x 4)
-    mops = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"][0]
-    out = os.path.join(ROOT, "profiles", "canvas_attn_l8k_mfma.txt")
+    mops = c[MOPS_COUNTER[dtype]][0]
+    tag = PROFILE_TAG[dtype]
+    out = os.path.join(ROOT, "profiles", f"{tag}_mfma.txt")
     with open(out, "w") as f:
-        f.write("# MFMA work of the canvas attention kernel (canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)\n")
+        f.write(f"# MFMA work of the canvas attention kernel ({dtype}; canvas step, L=8192, B=1, Hq=16, "
+                "Hkv=8, D=128)\n")
         f.write("# from rocprofv3 --pmc runs (each in its own process) of\n")
-        f.write("#   python3 bench.py --steps 2 --warmup 1 --profile-steps\n")
+        f.write(f"#   python3 bench.py --steps 2 --warmup 1 --profile-steps{flag}\n")
         f.write("#   pass 1: SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_MFMA\n")
-        f.write("#   pass 2: SQ_INSTS_VALU_MFMA_MOPS_BF16\n")
+        f.write(f"#   pass 2: {MOPS_COUNTER[dtype]}\n")
         f.write("# per-dispatch means over the dispatches of the kernel; written by\n")
-        f.write("#   python3 bench.py --summarize-mfma PASS1 PASS2 profiles/canvas_attn_l8k_kernel_trace.txt\n")
+        f.write(f"#   python3 bench.py --summarize-mfma PASS1 PASS2 profiles/{tag}_kernel_trace.txt{flag}\n")
         f.write(f"kernel: {ATTN_KERNEL}...>\n")
         f.write(f"kernel_source_hash: {kernel_source_hash()}\n")
         f.write(f"dispatches: {c['SQ_INSTS_MFMA'][1]}\n")
         f.write(f"mfma_instructions: {c['SQ_INSTS_MFMA'][0]:.0f}\n")
-        f.write(f"mfma_flop (MOPS_BF16 x 512): {mops * 512:.4e}\n")
+        f.write(f"mfma_flop ({MOPS_COUNTER[dtype][20:]} x 512): {mops * 512:.4e}\n")
         f.write(f"algorithmic_flop: {step_flops(1, 16, 8192, 128):.4e}\n")
         f.write(f"mfma_busy_cycles_per_simd: {busy:.0f}\n")
         if avg_us:
@@ -184,13 +203,16 @@ def summarize_mfma(pass1_dir, pass2_dir, trace_txt):
     print(open(out).read())
 
 
-def summarize_trace(stats_csv, out_txt):
+def summarize_trace(stats_csv, out_txt, dtype="bf16"):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     keep = [r for r in rows if "dg::" in r["Name"] or "copyBuffer" in r["Name"]]
+    flag = "" if dtype == "bf16" else f" --dtype {dtype}"
     lines = ["# rocprofv3 --kernel-trace --stats summary (kernels of this library)",
              "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-             "-d <dir> -o run -- python3 <repo>/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+             f"-d <dir> -o run -- python3 <repo>/bench.py --steps 10 --warmup 2 --no-cpu-baseline{flag}",
+             "# (written by: python3 bench.py --summarize-trace <dir>/run_kernel_stats.csv OUT"
+             f"{flag})",
              f"{'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_pct':>9}  kernel"]
     for r in keep:
         lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.3f} "
@@ -209,9 +231,179 @@ def commit_flops(B, Hq, L, D, Nc=256):
     return 4.0 * B * Hq * D * (Nc * L + Nc * (Nc + 1) / 2)
 
 
-def step_bytes(B, Hq, Hkv, L, D, Nc=256):
-    # cache K and V once, canvas Q/K/V, output
-    return 2.0 * B * (2 * L * Hkv * D + Nc * Hq * D + 2 * Nc * Hkv * D + Nc * Hq * D)
+def step_bytes(B, Hq, Hkv, L, D, esz=2, Nc=256):
+    # cache K and V once, canvas Q/K/V (esz bytes per element), bf16 output
+    return B * (esz * (2 * L * Hkv * D + Nc * Hq * D + 2 * Nc * Hkv * D) + 2.0 * Nc * Hq * D)
+
+
+def dev(a):
+    """numpy -> GPU tensor (uint16 bf16 bits or uint8 e4m3 bytes)."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda().view(torch.float8_e4m3fn)
+
+
+class Cycle:
+    """Device inputs of the L=8192 block cycle in one storage format."""
+
+    def __init__(self, dtype, name="cycle_l8k"):
+        import torch
+        import canvas_attention_amd.dg as dg
+        from canvas_attention_amd import synth
+        self.dg, self.dtype = dg, dtype
+        w = synth.WORKLOADS[name]
+        self.B, self.Hq, self.Hkv, self.D = w["batch"], w["hq"], w["hkv"], w["d"]
+        seed, self.n_steps = w["seed"], w["steps"]
+        self.L = synth.prefix_lengths(name)
+        self.Lv = int(self.L[0])
+        cap = self.Lv + 256
+        kc, vc = synth.cache(seed, self.L, cap, self.Hkv, self.D, dtype)
+        self.kc, self.vc = dev(kc), dev(vc)
+        canv = [synth.canvas(seed, self.B, self.Hq, self.Hkv, self.D, dtype, step=s)
+                for s in range(self.n_steps)]
+        self.qs = dev(np.stack([c[0] for c in canv]))
+        self.ks = dev(np.stack([c[1] for c in canv]))
+        self.vs = dev(np.stack([c[2] for c in canv]))
+        self.qb, self.kb, self.vb = (dev(x) for x in synth.block(seed, self.B, self.Hq, self.Hkv,
+                                                                 self.D, dtype))
+        self.out_steps = torch.empty(self.qs.shape, dtype=torch.bfloat16, device="cuda")
+        self.out_blk = torch.empty(self.qb.shape, dtype=torch.bfloat16, device="cuda")
+        self.ws = dg.alloc_workspace(self.qs[0], self.Hkv, cap)
+
+    def steps(self):
+        self.dg.canvas_step_loop(self.qs, self.ks, self.vs, self.kc, self.vc, self.L,
+                                 out=self.out_steps, workspace=self.ws)
+
+    def commit(self):
+        self.dg.commit_block(self.qb, self.kb, self.vb, self.kc, self.vc, self.L,
+                             out=self.out_blk, workspace=self.ws)
+
+    def one_step(self, i):
+        s = i % self.n_steps
+        self.dg.canvas_attn(self.qs[s], self.kc, self.vc, self.L, self.ks[s], self.vs[s],
+                            out=self.out_steps[s], workspace=self.ws)
+
+
+def call_medians(cy, reps, modes=("warm", "cold")):
+    """Per-launch kernel durations (the library's events around each launch),
+    median over calls of one canvas step (attention + merge): warm (the fixed
+    cache stays in the 256 MB last-level cache, as in a block's step loop) and
+    cold (a 512 MB scratch fill before every call, outside the timed kernels)."""
+    import torch
+    dg = cy.dg
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if "cold" in modes else None
+    medians = {}
+    for mode in modes:
+        dg.kernel_timing_read()
+        dg.kernel_timing_enable(True)
+        for i in range(reps):
+            if mode == "cold":
+                flush.fill_(i & 255)
+            cy.one_step(i)
+        a_ms, m_ms = dg.kernel_timing_samples(reps)
+        dg.kernel_timing_enable(False)
+        m_ms = m_ms if len(m_ms) == len(a_ms) else [0.0] * len(a_ms)
+        medians[mode] = {"attn": round(float(np.median(a_ms)) * 1e3, 3),
+                         "step": round(float(np.median(np.add(a_ms, m_ms))) * 1e3, 3)}
+    del flush
+    return medians
+
+
+def measure(dtype, steps, warmup, profile_steps=False):
+    """Times the block cycle in one format; returns the bench fields."""
+    import torch
+    cy = Cycle(dtype)
+    dg = cy.dg
+    B, Hq, Hkv, D, Lv, n_steps = cy.B, cy.Hq, cy.Hkv, cy.D, cy.Lv, cy.n_steps
+    stream = torch.cuda.current_stream()
+
+    def cycle():
+        cy.steps()
+        cy.commit()
+
+    for _ in range(warmup):
+        cycle()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        cycle()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    if profile_steps:
+        return {"ms_per_step": ms}
+
+    fl_step = step_flops(B, Hq, Lv, D)
+    fl_commit = commit_flops(B, Hq, Lv, D)
+    fl_cycle = n_steps * fl_step + fl_commit
+    peak = PEAK_TFLOPS[dtype]
+
+    # per-kernel durations: a second pass over the same canvas steps with the
+    # library's HIP events around every launch (same stream as the launches)
+    dg.kernel_timing_read()
+    dg.kernel_timing_enable(True)
+    for _ in range(steps):
+        cy.steps()
+    n_attn, attn_ms, n_merge, merge_ms = dg.kernel_timing_read()
+    for _ in range(steps):
+        cy.commit()
+    n_cattn, cattn_ms, n_cmerge, cmerge_ms = dg.kernel_timing_read()
+    dg.kernel_timing_enable(False)
+    attn_us = attn_ms / max(n_attn, 1) * 1e3
+    merge_us = merge_ms / max(n_merge, 1) * 1e3 if n_merge else 0.0
+    achieved = fl_step / (attn_us * 1e-6) / 1e12
+
+    # canvas steps alone (whole step incl. merge), for positions/s
+    t0.record(stream)
+    for _ in range(steps):
+        cy.steps()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / (steps * n_steps)
+    reps = max(steps, 50)
+    medians = call_medians(cy, reps)
+    kname = ATTN_KERNELS[dtype].replace(", ", ",")
+    return {
+        "value": round(fl_cycle / (ms * 1e-3) / 1e12, 2),
+        "ms_per_step": round(ms, 5),
+        "canvas_step_us": round(step_ms * 1e3, 3),
+        "canvas_step_tflops": round(fl_step / (step_ms * 1e-3) / 1e12, 2),
+        "canvas_positions_per_s": round(B * 256 / (step_ms * 1e-3), 1),
+        "canvas_step_mfma_frac": round(fl_step / (step_ms * 1e-3) / 1e12 / peak, 4),
+        "canvas_call_us_median": {"warm": medians["warm"], "cold": medians["cold"],
+                                  "calls": reps},
+        "kernels_us": {"canvas_attn": round(attn_us, 3), "canvas_merge": round(merge_us, 3),
+                       "commit_attn": round(cattn_ms / max(n_cattn, 1) * 1e3, 3),
+                       "commit_merge": round(cmerge_ms / max(n_cmerge, 1) * 1e3, 3)
+                       if n_cmerge else 0.0},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(dtype),
+                     "kernel": f"{kname}> (canvas step, L=8192)",
+                     "algorithmic_flop_per_launch": fl_step,
+                     "hbm_frac": round(step_bytes(B, Hq, Hkv, Lv, D, ELEM_BYTES[dtype])
+                                       / (attn_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "_config": {"batch": B, "prefix_len": Lv, "n_canvas": 256, "n_heads_q": Hq,
+                    "n_heads_kv": Hkv, "head_dim": D, "steps_per_block": n_steps},
+    }
+
+
+def fp8_summary(reps=100):
+    """The fp8 canvas step at L=8192 (warm median per call) for the bf16 line."""
+    cy = Cycle("fp8")
+    for i in range(10):
+        cy.one_step(i)
+    med = call_medians(cy, reps, modes=("warm",))["warm"]
+    fl = step_flops(cy.B, cy.Hq, cy.Lv, cy.D)
+    return {"canvas_attn_us": med["attn"], "canvas_step_us": med["step"],
+            "canvas_attn_tflops": round(fl / (med["attn"] * 1e-6) / 1e12, 2),
+            "frac_of_fp8_peak": round(fl / (med["attn"] * 1e-6) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+            "kernel": "attn_fp8_kernel<128,false>", "timing": f"median of {reps} calls, warm"}
 
 
 def main():
@@ -219,6 +411,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--dtype", choices=("bf16", "fp8"), default="bf16",
+                    help="storage format of q, K and V (fp8: OCP e4m3, tensor scales 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
@@ -230,18 +424,18 @@ def main():
                                                               "COPY_WRITE", "COPY_MIB"),
                     help="write the traffic file from four rocprofv3 --pmc output folders")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("PASS1", "PASS2", "TRACE_TXT"),
-                    help="write profiles/canvas_attn_l8k_mfma.txt from two rocprofv3 --pmc runs")
+                    help="write profiles/<tag>_mfma.txt from two rocprofv3 --pmc runs")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "OUT_TXT"),
                     help="write a kernel summary from a rocprofv3 --stats kernel_stats.csv")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, dtype=args.dtype)
         return
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace)
+        summarize_trace(*args.summarize_trace, dtype=args.dtype)
         return
     if args.summarize_mfma:
-        summarize_mfma(*args.summarize_mfma)
+        summarize_mfma(*args.summarize_mfma, dtype=args.dtype)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the canvas "
@@ -254,148 +448,36 @@ def main():
         copy_probe(args.copy_probe)
         return
 
-    import canvas_attention_amd.dg as dg
-    from canvas_attention_amd import synth
-
     torch.cuda.set_device(0)
-    name = "cycle_l8k"
-    w = synth.WORKLOADS[name]
-    B, Hq, Hkv, D, seed = w["batch"], w["hq"], w["hkv"], w["d"], w["seed"]
-    n_steps = w["steps"]
-    L = synth.prefix_lengths(name)
-    Lv = int(L[0])
-    cap = Lv + 256
-
-    def dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-
-    kc, vc = synth.cache(seed, L, cap, Hkv, D, "bf16")
-    kc_d, vc_d = dev(kc), dev(vc)
-    canv = [synth.canvas(seed, B, Hq, Hkv, D, "bf16", step=s) for s in range(n_steps)]
-    qs = torch.stack([dev(c[0]) for c in canv])
-    ks = torch.stack([dev(c[1]) for c in canv])
-    vs = torch.stack([dev(c[2]) for c in canv])
-    qb, kb, vb = (dev(x) for x in synth.block(seed, B, Hq, Hkv, D, "bf16"))
-    out_steps = torch.empty_like(qs)
-    out_blk = torch.empty_like(qb)
-    ws = dg.alloc_workspace(qs[0], Hkv, cap)
-    stream = torch.cuda.current_stream()
-
-    def cycle():
-        dg.canvas_step_loop(qs, ks, vs, kc_d, vc_d, L, out=out_steps, workspace=ws)
-        dg.commit_block(qb, kb, vb, kc_d, vc_d, L, out=out_blk, workspace=ws)
-
-    for _ in range(args.warmup):
-        cycle()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
-        cycle()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    m = measure(args.dtype, args.steps, args.warmup, args.profile_steps)
     if args.profile_steps:
-        print(json.dumps({"ms_per_step": ms}), flush=True)
+        print(json.dumps(m), flush=True)
         return
-
-    fl_step = step_flops(B, Hq, Lv, D)
-    fl_commit = commit_flops(B, Hq, Lv, D)
-    fl_cycle = n_steps * fl_step + fl_commit
-    value = fl_cycle / (ms * 1e-3) / 1e12
-
-    # per-kernel durations: a second pass over the same canvas steps with the
-    # library's HIP events around every launch (same stream as the launches)
-    dg.kernel_timing_read()
-    dg.kernel_timing_enable(True)
-    for _ in range(args.steps):
-        dg.canvas_step_loop(qs, ks, vs, kc_d, vc_d, L, out=out_steps, workspace=ws)
-    n_attn, attn_ms, n_merge, merge_ms = dg.kernel_timing_read()
-    for _ in range(args.steps):
-        dg.commit_block(qb, kb, vb, kc_d, vc_d, L, out=out_blk, workspace=ws)
-    n_cattn, cattn_ms, n_cmerge, cmerge_ms = dg.kernel_timing_read()
-    dg.kernel_timing_enable(False)
-    attn_us = attn_ms / max(n_attn, 1) * 1e3
-    merge_us = merge_ms / max(n_merge, 1) * 1e3 if n_merge else 0.0
-    achieved = fl_step / (attn_us * 1e-6) / 1e12
-
-    # canvas steps alone (whole step incl. merge), for positions/s
-    t0.record(stream)
-    for _ in range(args.steps):
-        dg.canvas_step_loop(qs, ks, vs, kc_d, vc_d, L, out=out_steps, workspace=ws)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / (args.steps * n_steps)
-
-    # per-launch kernel durations (the library's events around each launch), median
-    # over calls of one canvas step (attention + merge): warm (the fixed cache stays
-    # in the 256 MB last-level cache, as in a block's step loop) and cold (a 512 MB
-    # scratch fill before every call, outside the timed kernels)
-    reps = max(args.steps, 50)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-
-    def one_step(i):
-        s = i % n_steps
-        dg.canvas_attn(qs[s], kc_d, vc_d, L, ks[s], vs[s], out=out_steps[s], workspace=ws)
-
-    medians = {}
-    for mode in ("warm", "cold"):
-        dg.kernel_timing_read()
-        dg.kernel_timing_enable(True)
-        for i in range(reps):
-            if mode == "cold":
-                flush.fill_(i & 255)
-            one_step(i)
-        a_ms, m_ms = dg.kernel_timing_samples(reps)
-        dg.kernel_timing_enable(False)
-        m_ms = m_ms if len(m_ms) == len(a_ms) else [0.0] * len(a_ms)
-        medians[mode] = {"attn": round(float(np.median(a_ms)) * 1e3, 3),
-                         "step": round(float(np.median(np.add(a_ms, m_ms))) * 1e3, 3)}
-    del flush
-
+    cfg = m.pop("_config")
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": m.pop("value"),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": m.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
-        "config": {"workload": "block cycle: 12 canvas steps + commit at prefix L=8192",
-                   "batch": B, "prefix_len": Lv, "n_canvas": 256, "n_heads_q": Hq,
-                   "n_heads_kv": Hkv, "head_dim": D, "steps_per_block": n_steps},
-        "canvas_step_us": round(step_ms * 1e3, 3),
-        "canvas_step_tflops": round(fl_step / (step_ms * 1e-3) / 1e12, 2),
-        "canvas_positions_per_s": round(B * 256 / (step_ms * 1e-3), 1),
-        "canvas_step_mfma_frac": round(fl_step / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "canvas_call_us_median": {"warm": medians["warm"], "cold": medians["cold"],
-                                  "calls": reps},
-        "kernels_us": {"canvas_attn": round(attn_us, 3), "canvas_merge": round(merge_us, 3),
-                       "commit_attn": round(cattn_ms / max(n_cattn, 1) * 1e3, 3),
-                       "commit_merge": round(cmerge_ms / max(n_cmerge, 1) * 1e3, 3)
-                       if n_cmerge else 0.0},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "attn_bf16_kernel<128,false> (canvas step, L=8192)",
-                     "algorithmic_flop_per_launch": fl_step,
-                     "hbm_frac": round(step_bytes(B, Hq, Hkv, Lv, D) / (attn_us * 1e-6) / 1e9
-                                       / PEAK_HBM_GBS, 4)},
+        "config": {"workload": "block cycle: 12 canvas steps + commit at prefix L=8192", **cfg},
+        **m,
     }
-
+    if args.dtype == "bf16":
+        result["fp8"] = fp8_summary()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(name, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline("cycle_l8k", args.cpu_seconds, args.dtype)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(name, budget_s):
+def cpu_baseline(name, budget_s, dtype="bf16"):
     """The CPU fp64 oracle on a bounded sample of the same workload: whole canvas
     steps of the block cycle (each with its own seeded canvas Q/K/V, all 256
     positions and all heads), one after another until the time budget is spent."""
@@ -405,8 +487,8 @@ def cpu_baseline(name, budget_s):
     B, Hq, Hkv, D, seed = w["batch"], w["hq"], w["hkv"], w["d"], w["seed"]
     L = synth.prefix_lengths(name)
     Lv = int(L[0])
-    kc, vc = synth.cache(seed, L, Lv + 256, Hkv, D, "bf16")
-    steps = [synth.canvas(seed, B, Hq, Hkv, D, "bf16", step=s) for s in range(w["steps"])]
+    kc, vc = synth.cache(seed, L, Lv + 256, Hkv, D, dtype)
+    steps = [synth.canvas(seed, B, Hq, Hkv, D, dtype, step=s) for s in range(w["steps"])]
     done = 0
     t_start = time.perf_counter()
     elapsed = 0.0
