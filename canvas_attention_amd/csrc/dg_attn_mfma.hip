@@ -91,7 +91,7 @@ struct FmtBf16 {
   static constexpr float kBias = 0.f;        // exponent offset of the exponentials
 };
 // e4m3 tops out at 448 (just under 2^8.81), and the gfx950 conversion returns NaN
-// rather than saturating from 464 up, so the exponentials that become the B
+// rather than saturating above 464, so the exponentials that become the B
 // operand of the value MFMA must stay below that: a bias of 5 plus a threshold of
 // 3.5 bounds them by 2^8.5.  The bias also lifts the bulk of a diffuse row (2^-6 ..
 // 2^-10 of its max) into e4m3's normal range, where the rounding error is 2^-4
