@@ -589,6 +589,9 @@ struct Ops8 {
   i32x8 p;        // B operand: lane (n, h), byte 16t + i holds the e4m3 exponential of
                   // query n and key 32t + 16h + i
   f32x16 s[2];    // scores of the chunk the next softmax works on, per half
+  i32x8 ones;     // A operand of e4m3 ones (0x38): ones^T P^T sums the rounded weights
+  f32x16 rs;      // row sums of the rounded weights: every element of lane (n, h) holds
+                  // query n's sum over all keys so far (the MFMA adds over both halves)
 };
 
 // two 16-byte LDS reads joined into one 32-byte operand
@@ -661,7 +664,8 @@ __device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
 }
 
 // fp8 counterpart of prepare_scores: masking with the permuted key order, the
-// max of the chunk's 32 scores, and the lazy rescale with the exponent bias.
+// max of the chunk's 32 scores, and the lazy rescale with the exponent bias (the
+// row sums are rescaled with the outputs; only element 0 is ever read).
 template <int MB, bool CAUSAL>
 __device__ __forceinline__ void prepare_scores(Ops8& op, bool masked, int key0, int kstop, int L,
                                                int qi, int h, float c2, State<MB>& acc) {
@@ -682,7 +686,7 @@ __device__ __forceinline__ void prepare_scores(Ops8& op, bool masked, int key0, 
     const float alpha = __builtin_amdgcn_exp2f(acc.mlog - mnew);
     acc.mlog = mnew;
     acc.thr = (mnew + (FmtFp8::kBias + FmtFp8::kThreshold)) / c2;
-    acc.lsum *= alpha;
+    op.rs[0] *= alpha;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++)
 #pragma unroll
@@ -690,8 +694,11 @@ __device__ __forceinline__ void prepare_scores(Ops8& op, bool masked, int key0, 
   }
 }
 
-// exp2(s*c - m) of the 64 keys, summed in fp32 before rounding and packed to
-// e4m3 (v_cvt_pk_fp8_f32 writes two bytes, round to nearest even) in key order.
+// exp2(s*c - m) of the 64 keys, packed to e4m3 (v_cvt_pk_fp8_f32 writes two
+// bytes, round to nearest even) in key order.  The row sum is taken from the
+// rounded bytes by the value MFMAs (values below), so numerator and denominator
+// use the same weights: the output is a convex combination of the values, and a
+// row whose weight sits on one key is exact.
 template <int MB>
 __device__ __forceinline__ void numerators(Ops8& op, float c2, State<MB>& acc) {
   const float nm = -acc.mlog;
@@ -699,14 +706,6 @@ __device__ __forceinline__ void numerators(Ops8& op, float c2, State<MB>& acc) {
   for (int t = 0; t < 2; t++)
 #pragma unroll
     for (int i = 0; i < 16; i++) op.s[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(op.s[t][i], c2, nm));
-  float part[8];
-#pragma unroll
-  for (int q = 0; q < 8; q++) {
-    const f32x16& x = op.s[q >> 2];
-    const int b = 4 * (q & 3);
-    part[q] = (x[b] + x[b + 1]) + (x[b + 2] + x[b + 3]);
-  }
-  acc.lsum += ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
 #pragma unroll
   for (int w = 0; w < 8; w++) {
     const f32x16& x = op.s[w >> 2];
@@ -717,9 +716,10 @@ __device__ __forceinline__ void numerators(Ops8& op, float c2, State<MB>& acc) {
 }
 
 template <int MB>
-__device__ __forceinline__ void values(const Ops8& op, State<MB>& acc) {
+__device__ __forceinline__ void values(Ops8& op, State<MB>& acc) {
 #pragma unroll
   for (int mb = 0; mb < MB; mb++) acc.o[mb] = mfma_f8(op.v[mb], op.p, acc.o[mb]);
+  op.rs = mfma_f8(op.ones, op.p, op.rs);
 }
 
 // The kernel.  Wave (rg, kg) processes chunk k = tile k*WK + kg of the unit for
@@ -908,6 +908,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const Plan& plan) {
   Ops op;
   if constexpr (F8) {
 #pragma unroll
+    for (int i = 0; i < 8; i++) op.ones[i] = 0x38383838;  // e4m3 1.0 in every byte
+#pragma unroll
+    for (int i = 0; i < 16; i++) op.rs[i] = 0.f;
+#pragma unroll
     for (int ks = 0; ks < 2; ks++)
 #pragma unroll
       for (int part = 0; part < 2; part++) kaddr[ks][part] = lring + kg * TILEB + lo.k[ks][part];
@@ -1012,6 +1016,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const Plan& plan) {
   // From here on the ring is free: every operand read and every stage load was
   // waited for at barrier nstages-1 at the latest (group 1's last Y, after it,
   // reads nothing).
+  // fp8: both lanes of a query hold its whole row sum; half 0 carries it into the
+  // additive per-lane sums of the merge below.
+  if constexpr (F8) acc.lsum = h == 0 ? op.rs[0] : 0.f;
 
   // ---- merge the key groups through LDS: key groups 1.. leave their state,
   //      group 0 folds it into its own and writes the rows (one barrier)
