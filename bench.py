@@ -194,8 +194,11 @@ def summarize_mfma(pass1_dir, pass2_dir, trace_txt, dtype="bf16"):
         f.write(f"kernel_source_hash: {kernel_source_hash()}\n")
         f.write(f"dispatches: {c['SQ_INSTS_MFMA'][1]}\n")
         f.write(f"mfma_instructions: {c['SQ_INSTS_MFMA'][0]:.0f}\n")
-        f.write(f"mfma_flop ({MOPS_COUNTER[dtype][20:]} x 512): {mops * 512:.4e}\n")
+        f.write(f"mfma_flop ({MOPS_COUNTER[dtype][19:]} x 512): {mops * 512:.4e}\n")
         f.write(f"algorithmic_flop: {step_flops(1, 16, 8192, 128):.4e}\n")
+        f.write(f"mfma_flop / algorithmic_flop: {mops * 512 / step_flops(1, 16, 8192, 128):.4f}"
+                + (" (the fp8 kernel adds one row-sum MFMA per 8 score and value MFMAs)\n"
+                   if dtype == "fp8" else "\n"))
         f.write(f"mfma_busy_cycles_per_simd: {busy:.0f}\n")
         if avg_us:
             f.write(f"kernel_avg_us (kernel trace): {avg_us}\n")
