@@ -27,6 +27,9 @@ import numpy as np
 N_CANVAS = 256
 
 T_CACHE_K, T_CACHE_V, T_Q, T_K, T_V, T_QB, T_KB, T_VB = range(8)
+T_LOGITS, T_NOISE, T_PEAK = 8, 9, 10   # canvas sampler inputs
+
+VOCAB = 262144  # vocabulary of the sampled model family ("262k vocabulary")
 
 # Workloads, named by what they are.  "steps": canvas steps per block,
 # "blocks": consecutive blocks (each = steps + one commit).
@@ -151,3 +154,30 @@ def block(seed: int, batch: int, hq: int, hkv: int, d: int, dtype: str, block: i
     k = batched(seed, T_KB, batch, N_CANVAS, hkv, d, dtype, block)
     v = batched(seed, T_VB, batch, N_CANVAS, hkv, d, dtype, block)
     return q, k, v
+
+
+def sampler_logits(seed: int, batch: int, vocab: int = VOCAB, step: int = 0) -> np.ndarray:
+    """bf16 logits [B, 256, V] of one denoising step, for the canvas sampler.
+
+    Every position gets N(0,1) logits plus, at one uniformly drawn token, a peak
+    whose height is uniform in [0, 24]: from near-uniform positions (entropy
+    close to ln V) to near-certain ones (entropy near 0), as in a canvas that is
+    partly resolved."""
+    out = np.empty((batch, N_CANVAS, vocab), np.uint16)
+    for b in range(batch):
+        rng = np.random.default_rng([seed, T_LOGITS, b, 0, step])
+        x = rng.standard_normal(size=(N_CANVAS, vocab), dtype=np.float32)
+        pk = np.random.default_rng([seed, T_PEAK, b, 0, step])
+        tok = pk.integers(0, vocab, N_CANVAS)
+        x[np.arange(N_CANVAS), tok] += pk.uniform(0.0, 24.0, N_CANVAS).astype(np.float32)
+        out[b] = bf16_round(x)
+    return out
+
+
+def noise_tokens(seed: int, batch: int, vocab: int = VOCAB, step: int = 0) -> np.ndarray:
+    """Uniformly random tokens [B, 256] (int32) for the re-noised positions."""
+    out = np.empty((batch, N_CANVAS), np.int32)
+    for b in range(batch):
+        rng = np.random.default_rng([seed, T_NOISE, b, 0, step])
+        out[b] = rng.integers(0, vocab, N_CANVAS, dtype=np.int64).astype(np.int32)
+    return out
