@@ -382,6 +382,49 @@ dg_status dg_canvas_step_loop(const dg_shape* shape, int32_t n_steps, const void
   return DG_OK;
 }
 
+dg_status dg_canvas_sample(const dg_sample_shape* shape, const void* logits,
+                           const int32_t* noise_tokens, const int32_t* prev_argmax,
+                           float* entropy, int32_t* argmax, int32_t* tokens,
+                           int32_t* accepted, int32_t* stop, void* stream) {
+  if (!shape) return fail(DG_ERR_NULL, "shape is NULL");
+  if (shape->batch < 1 || shape->batch > DG_MAX_BATCH)
+    return fail(DG_ERR_SHAPE, "batch %d outside 1..%d", shape->batch, DG_MAX_BATCH);
+  if (shape->n_canvas != DG_N_CANVAS)
+    return fail(DG_ERR_SHAPE, "n_canvas %d, must be %d", shape->n_canvas, DG_N_CANVAS);
+  if (shape->vocab < 8 || shape->vocab % 8 != 0 || shape->vocab > (1 << 27))
+    return fail(DG_ERR_SHAPE, "vocab %d: a multiple of 8 in 8..2^27", shape->vocab);
+  if (!(shape->tau > 0.f) || isinf(shape->tau))
+    return fail(DG_ERR_SHAPE, "tau must be finite and > 0");
+  if (!(shape->budget >= 0.f) || shape->budget > 1e6f)
+    return fail(DG_ERR_SHAPE, "budget must be in 0..1e6");
+  if (!(shape->stop_entropy >= 0.f) || shape->stop_entropy > 1e6f)
+    return fail(DG_ERR_SHAPE, "stop_entropy must be in 0..1e6");
+  if (!logits || !noise_tokens || !entropy || !argmax || !tokens || !accepted || !stop)
+    return fail(DG_ERR_NULL, "a required argument is NULL (only prev_argmax may be)");
+  if (!aligned16(logits)) return fail(DG_ERR_ALIGN, "logits %p is not 16-byte aligned", logits);
+  const void* words[] = {noise_tokens, prev_argmax, entropy, argmax, tokens, accepted, stop};
+  for (const void* p : words)
+    if (((uintptr_t)p & 3u) != 0) return fail(DG_ERR_ALIGN, "pointer %p is not 4-byte aligned", p);
+  dg::SampleArgs a;
+  a.logits = logits;
+  a.noise = noise_tokens;
+  a.prev = prev_argmax;
+  a.entropy = entropy;
+  a.argmax = argmax;
+  a.tokens = tokens;
+  a.accepted = accepted;
+  a.stop = stop;
+  a.qbudget = llrint((double)shape->budget * 4294967296.0);
+  a.qstop = llrint((double)shape->stop_entropy * 4294967296.0);
+  a.c = (float)(1.4426950408889634 / (double)shape->tau);
+  a.vocab = shape->vocab;
+  a.batch = shape->batch;
+  const int err = dg::launch_sample(a, stream);
+  if (err != 0)
+    return fail(DG_ERR_HIP, "sampler launch failed: %s", hipGetErrorString((hipError_t)err));
+  return DG_OK;
+}
+
 const char* dg_status_string(dg_status status) {
   switch (status) {
     case DG_OK: return "DG_OK";

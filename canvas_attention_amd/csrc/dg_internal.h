@@ -76,12 +76,30 @@ struct AttnArgs {
   float out_scale;      // fp8: the v scale, applied with the normalisation (else 1)
 };
 
+// Canvas sampler (dg_sample.hip).
+struct SampleArgs {
+  const void* logits;      // [B][256][V] bf16
+  const int32_t* noise;    // [B][256] re-noise tokens
+  const int32_t* prev;     // [B][256] previous step's argmax, or null
+  float* entropy;          // [B][256] out, nats
+  int32_t* argmax;         // [B][256] out
+  int32_t* tokens;         // [B][256] out
+  int32_t* accepted;       // [B][256] out, 0/1
+  int32_t* stop;           // [B] out, 0/1
+  long long qbudget;       // budget in units of 2^-32 nats
+  long long qstop;         // stop threshold in units of 2^-32 nats
+  float c;                 // log2(e) / tau
+  int32_t vocab;
+  int32_t batch;
+};
+
 // Host-side launchers (defined next to their kernels).  Each returns the HIP
 // error of the launch.
 int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream);
 int launch_attn_fp8(const AttnArgs& a, const Plan& p, bool causal, void* stream);
 int launch_attn_f32(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream);
 int launch_merge(const AttnArgs& a, const Plan& p, int head_dim, bool bf16_out, void* stream);
+int launch_sample(const SampleArgs& s, void* stream);
 
 // Rows per unit of the fp32 kernel and the key granule of every kernel.
 constexpr int kRowsF32 = 64;

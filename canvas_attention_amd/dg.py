@@ -7,8 +7,8 @@ streams.  Importing this module raises if libdg.so has not been built -- there
 is no CPU fallback.
 
 Functions mirror the C entry points: ``canvas_attn``, ``commit_block``,
-``canvas_step_loop``, ``workspace_bytes``, ``kernel_timing_enable`` and
-``kernel_timing_read``.
+``canvas_step_loop``, ``canvas_sample``, ``workspace_bytes``,
+``kernel_timing_enable`` and ``kernel_timing_read``.
 """
 from __future__ import annotations
 
@@ -34,6 +34,12 @@ class DgShape(ctypes.Structure):
                 ("n_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("q_scale", ctypes.c_float),
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+
+
+class DgSampleShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_canvas", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("tau", ctypes.c_float), ("budget", ctypes.c_float),
+                ("stop_entropy", ctypes.c_float)]
 
 
 class DgKv(ctypes.Structure):
@@ -62,6 +68,8 @@ lib.dg_commit_block.restype = _i32
 lib.dg_canvas_step_loop.argtypes = [_P(DgShape), _i32, _vp, _i64, _P(DgKv), _i64, _P(DgKv), _vp,
                                     _vp, _i64, _vp, _sz, _vp]
 lib.dg_canvas_step_loop.restype = _i32
+lib.dg_canvas_sample.argtypes = [_P(DgSampleShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+lib.dg_canvas_sample.restype = _i32
 lib.dg_status_string.argtypes = [_i32]
 lib.dg_status_string.restype = ctypes.c_char_p
 lib.dg_last_error.argtypes = []
@@ -76,6 +84,7 @@ lib.dg_kernel_timing_samples.argtypes = [_P(ctypes.c_float), _P(ctypes.c_float),
 lib.dg_kernel_timing_samples.restype = _i32
 
 EXPORTS = ["dg_workspace_bytes", "dg_canvas_attn", "dg_commit_block", "dg_canvas_step_loop",
+           "dg_canvas_sample",
            "dg_status_string", "dg_last_error", "dg_kernel_timing_enable",
            "dg_kernel_timing_read", "dg_kernel_timing_samples"]
 
@@ -231,6 +240,37 @@ def canvas_step_loop(q_steps, k_steps, v_steps, k_cache, v_cache, prefix_len, ou
                                  _stream(stream))
     _check("dg_canvas_step_loop", st)
     return out
+
+
+def canvas_sample(logits, noise_tokens, prev_argmax=None, tau=0.8, budget=0.1,
+                  stop_entropy=0.005, out=None, stream=None):
+    """dg_canvas_sample: logits [B,256,V] bf16, noise_tokens and prev_argmax [B,256]
+    int32 (prev_argmax may be None).  Returns (entropy float32 [B,256], argmax,
+    tokens, accepted int32 [B,256], stop int32 [B]); `out` may supply those five
+    tensors."""
+    _need(logits, "logits", torch.bfloat16, 3)
+    B, Nc, V = logits.shape
+    _need(noise_tokens, "noise_tokens", torch.int32, 2)
+    if tuple(noise_tokens.shape) != (B, Nc):
+        raise ValueError("noise_tokens must be [B, 256]")
+    if prev_argmax is not None:
+        _need(prev_argmax, "prev_argmax", torch.int32, 2)
+        if tuple(prev_argmax.shape) != (B, Nc):
+            raise ValueError("prev_argmax must be [B, 256]")
+    if out is None:
+        dev = logits.device
+        out = (torch.empty(B, Nc, dtype=torch.float32, device=dev),
+               torch.empty(B, Nc, dtype=torch.int32, device=dev),
+               torch.empty(B, Nc, dtype=torch.int32, device=dev),
+               torch.empty(B, Nc, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    entropy, argmax, tokens, accepted, stop = out
+    shape = DgSampleShape(B, Nc, V, float(tau), float(budget), float(stop_entropy))
+    st = lib.dg_canvas_sample(ctypes.byref(shape), _ptr(logits), _ptr(noise_tokens),
+                              _ptr(prev_argmax), _ptr(entropy), _ptr(argmax), _ptr(tokens),
+                              _ptr(accepted), _ptr(stop), _stream(stream))
+    _check("dg_canvas_sample", st)
+    return entropy, argmax, tokens, accepted, stop
 
 
 def kernel_timing_enable(on: bool = True):

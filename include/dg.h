@@ -164,6 +164,45 @@ dg_status dg_canvas_step_loop(const dg_shape* shape, int32_t n_steps, const void
                               const int32_t* prefix_len, void* out, int64_t out_step_stride,
                               void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Canvas sampler ("DiffusionGemma Technical Report", paperfeed.app summary,
+ * section "The mechanism: an AR model turned inside out", sampler paragraph).
+ * After a denoising step, for every sequence b and canvas position i:
+ *   entropy[b,i] = -sum_v q_v ln q_v,  q = softmax(logits[b,i,:] / tau)   (nats)
+ *   argmax[b,i]  = the lowest v with the largest logit
+ * Positions are then taken in ascending (entropy, i) order and accepted while the
+ * cumulative entropy of the accepted ones stays <= budget (possibly none);
+ *   tokens[b,i] = accepted ? argmax[b,i] : noise_tokens[b,i]
+ * (noise_tokens: the caller's uniformly random tokens for re-noised positions),
+ * and stop[b] = 1 iff the mean entropy of the canvas is < stop_entropy and every
+ * argmax equals prev_argmax (the previous step's argmax; NULL: no previous step,
+ * stop = 0).  The acceptance and stop decisions count each fp32 entropy as an
+ * integer number of 2^-32 nats, so the cumulative sums are exact and do not
+ * depend on any summation order.
+ *   logits        [B][Nc][V] bf16 device, 16-byte aligned; V a multiple of 8,
+ *                 8 <= V <= 2^27; finite or -inf (masked) values, one finite
+ *                 value per row
+ *   noise_tokens, prev_argmax [B][Nc] int32 device (prev_argmax may be NULL)
+ *   entropy       [B][Nc] float device (out); argmax, tokens, accepted (0/1)
+ *                 [B][Nc] int32 device (out); stop [B] int32 device (out)
+ * Two kernel launches on `stream`; no workspace.  The tempered logits the report
+ * anneals (tau from 0.8 to 0.4 over the steps) are the caller's schedule: tau is
+ * per call.
+ */
+typedef struct {
+  int32_t batch;        /* B, 1..DG_MAX_BATCH                                     */
+  int32_t n_canvas;     /* Nc, must equal DG_N_CANVAS                             */
+  int32_t vocab;        /* V                                                      */
+  float tau;            /* temperature, > 0                                       */
+  float budget;         /* cumulative entropy budget in nats, 0..1e6 (report: 0.1) */
+  float stop_entropy;   /* mean-entropy threshold in nats, 0..1e6 (report: 0.005)  */
+} dg_sample_shape;
+
+dg_status dg_canvas_sample(const dg_sample_shape* shape, const void* logits,
+                           const int32_t* noise_tokens, const int32_t* prev_argmax,
+                           float* entropy, int32_t* argmax, int32_t* tokens,
+                           int32_t* accepted, int32_t* stop, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* dg_status_string(dg_status status);
 

@@ -48,7 +48,9 @@ def row_entropy(logits_row: np.ndarray, tau: float) -> float:
     z = e.sum()
     q = e / z
     lq = (x - m) - np.log(z)          # ln q, exact form (no log of a rounded q)
-    return float(-(q * lq).sum())
+    # 0 ln 0 = 0: tokens with -inf logits (masked) have q = 0 and add nothing
+    pos = q > 0
+    return float(-(q[pos] * lq[pos]).sum())
 
 
 def row_stats(logits: np.ndarray, tau: float):

@@ -156,3 +156,32 @@ def test_status_strings(dg):
     for code, name in dg.STATUS.items():
         assert dg.lib.dg_status_string(code).decode() == name
     assert dg.lib.dg_status_string(-99).decode() == "DG_ERR_UNKNOWN"
+
+
+def sample_shape(dg, **kw):
+    d = dict(batch=1, n_canvas=256, vocab=262144, tau=0.8, budget=0.1, stop_entropy=0.005)
+    d.update(kw)
+    return dg.DgSampleShape(**d)
+
+
+def call_sample(dg, sh, logits=FAKE, noise=FAKE, prev=None, outs=(FAKE, FAKE, FAKE, FAKE, FAKE)):
+    return dg.lib.dg_canvas_sample(ctypes.byref(sh), logits, noise, prev, *outs, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), -2), (dict(batch=65), -2), (dict(n_canvas=255), -2),
+    (dict(vocab=4), -2), (dict(vocab=1001), -2), (dict(vocab=(1 << 27) + 8), -2),
+    (dict(tau=0.0), -2), (dict(tau=float("inf")), -2), (dict(tau=float("nan")), -2),
+    (dict(budget=-0.1), -2), (dict(budget=float("nan")), -2), (dict(stop_entropy=-1.0), -2),
+])
+def test_sample_shape_errors(dg, kw, code):
+    assert call_sample(dg, sample_shape(dg, **kw)) == code, dg.lib.dg_last_error()
+
+
+def test_sample_null_and_alignment(dg):
+    sh = sample_shape(dg)
+    assert call_sample(dg, sh, logits=None) == -1
+    assert call_sample(dg, sh, noise=None) == -1
+    assert call_sample(dg, sh, outs=(FAKE, None, FAKE, FAKE, FAKE)) == -1
+    assert call_sample(dg, sh, logits=FAKE + 8) == -7
+    assert call_sample(dg, sh, prev=FAKE + 2) == -7

@@ -1,0 +1,128 @@
+"""GPU parity of the canvas sampler (dg_canvas_sample) against oracle/sampler.py.
+
+The sampler follows "DiffusionGemma Technical Report" (paperfeed.app summary),
+section "The mechanism: an AR model turned inside out", sampler paragraph.
+
+Gates:
+  * argmax: bit-exact (ties to the lowest token);
+  * entropy: |gpu - oracle| <= 1e-6 + 3e-5 * H (nats).  The kernel works in fp32:
+    one rounding of each exponent argument (relative 2^-24 of |y| <= 16 inside
+    the lazy window), exp2 to about 1 ulp, and sums of 64 terms per lane and
+    batch plus 8 batches and 9 merge levels (relative error of z and s well
+    below 1e-5); H = log2(z) - s/z turns those into an absolute error of about
+    1e-7 near H = 0 and a relative one of order 1e-5 at H ~ 12;
+  * acceptance, tokens and stop: exact against the oracle's selection fed with
+    the GPU's own fp32 entropies (both sides decide in that precision, summing
+    entropies as integers of 2^-32 nats).
+"""
+import numpy as np
+import pytest
+
+from canvas_attention_amd import synth
+from helpers import to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU machines skip the module
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import canvas_attention_amd.dg as dg  # noqa: E402  (loads libdg.so; raises if missing)
+from oracle import sampler  # noqa: E402
+
+TOL_ABS, TOL_REL = 1e-6, 3e-5
+
+
+def run(logits, noise, prev=None, tau=0.8, budget=0.1, stop_entropy=0.005):
+    lg = to_dev(logits)
+    nz = torch.from_numpy(np.ascontiguousarray(noise, np.int32)).cuda()
+    pv = None if prev is None else torch.from_numpy(np.ascontiguousarray(prev, np.int32)).cuda()
+    H, am, tok, acc, stop = dg.canvas_sample(lg, nz, pv, tau, budget, stop_entropy)
+    torch.cuda.synchronize()
+    return H.cpu().numpy(), am.cpu().numpy(), tok.cpu().numpy(), acc.cpu().numpy(), stop.cpu().numpy()
+
+
+def check(logits, noise, prev=None, tau=0.8, budget=0.1, stop_entropy=0.005, rows=None):
+    H, am, tok, acc, stop = run(logits, noise, prev, tau, budget, stop_entropy)
+    sel = slice(None) if rows is None else rows
+    Hr, amr = sampler.row_stats(logits[:, sel], tau)
+    np.testing.assert_array_equal(am[:, sel], amr)
+    err = np.abs(H[:, sel] - Hr)
+    worst = float((err - (TOL_ABS + TOL_REL * Hr)).max())
+    assert worst <= 0, f"entropy error exceeds the gate by {worst:.3e}"
+    t2, a2, s2 = sampler.select(H, am, noise, prev, budget, stop_entropy)
+    np.testing.assert_array_equal(tok, t2)
+    np.testing.assert_array_equal(acc, a2)
+    np.testing.assert_array_equal(stop, s2)
+    return H, am, acc, stop, float(err.max()), float((err / np.maximum(Hr, 1e-30)).max())
+
+
+def test_sampler_full_vocab():
+    """One canvas over the 262144-token vocabulary, tau 0.8 (the start of the
+    report's annealing), every row against the oracle."""
+    lg = synth.sampler_logits(1006, 1)
+    nz = synth.noise_tokens(1006, 1)
+    H, am, acc, stop, e_abs, e_rel = check(lg, nz)
+    assert acc.sum() > 0 and stop.sum() == 0
+    print(f"V=262144: max |dH| {e_abs:.2e}, max rel {e_rel:.2e}, accepted {int(acc.sum())}")
+
+
+@pytest.mark.parametrize("tau", [0.4, 1.0])
+def test_sampler_temperatures(tau):
+    lg = synth.sampler_logits(1007, 1, step=1)
+    nz = synth.noise_tokens(1007, 1, step=1)
+    rows = np.arange(0, 256, 5)
+    check(lg, nz, tau=tau, rows=rows)
+
+
+@pytest.mark.parametrize("B,V", [(1, 8), (2, 1000), (1, 4096 * 8 + 8), (3, 65536 + 4096 * 3)])
+def test_sampler_vocab_sizes(B, V):
+    """Tails: vocabularies that are not whole batches of 4096 16-byte chunks."""
+    lg = synth.sampler_logits(1008, B, vocab=V)
+    nz = synth.noise_tokens(1008, B, vocab=V)
+    check(lg, nz, budget=0.5)
+
+
+def test_sampler_argmax_ties_and_masked_tokens():
+    rng = np.random.default_rng(9)
+    V = 50000
+    x = rng.standard_normal((1, 256, V)).astype(np.float32)
+    for i in range(256):  # the row max three times: the lowest index wins
+        pos = np.sort(rng.choice(V, 3, replace=False))
+        x[0, i, pos] = 9.0
+    mask = rng.random((1, 256, V)) < 0.3
+    x = np.where(mask, -np.inf, x).astype(np.float32)
+    x[0, :, 0] = 1.0  # keep the first token finite in every row
+    lg = synth.bf16_round(x)
+    nz = synth.noise_tokens(1009, 1, vocab=V)
+    H, am, acc, stop, _, _ = check(lg, nz)
+    assert np.isfinite(H).all()
+
+
+def test_sampler_stop_rule():
+    """A confident canvas: stop only with a previous step whose argmax matches."""
+    V = 32768
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((2, 256, V)).astype(np.float32)
+    tok = rng.integers(0, V, (2, 256))
+    for b in range(2):
+        x[b, np.arange(256), tok[b]] += 40.0
+    lg = synth.bf16_round(x)
+    nz = synth.noise_tokens(1010, 2, vocab=V)
+    H, am, _, _, _ = run(lg, nz)
+    assert (H < 1e-4).all()
+    prev = am.copy()
+    prev[1, 17] += 1  # canvas 1 changed one prediction
+    _, _, acc, stop, _, _ = check(lg, nz, prev=prev)
+    np.testing.assert_array_equal(stop, [1, 0])
+    _, _, _, stop2, _, _ = check(lg, nz, prev=None)
+    np.testing.assert_array_equal(stop2, [0, 0])
+
+
+def test_sampler_determinism():
+    lg = synth.sampler_logits(1011, 1, vocab=65536)
+    nz = synth.noise_tokens(1011, 1, vocab=65536)
+    a = run(lg, nz)
+    b = run(lg, nz)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)

@@ -101,3 +101,16 @@ def test_selection_is_the_longest_prefix():
             assert float(np.sum(H[b, order[:n + 1]], dtype=np.float64)) > 0.1 - 1e-6
         np.testing.assert_array_equal(tokens[b], np.where(acc[b] == 1, am[b], noise[b]))
     assert not stop.any()
+
+
+def test_masked_tokens_drop_out():
+    """-inf logits (masked tokens) carry q = 0: the entropy and argmax equal those
+    of the row without them."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(3000) * 2).astype(np.float32)
+    keep = rng.random(3000) < 0.7
+    masked = np.where(keep, x, -np.inf).astype(np.float32)
+    H1, am1 = sampler.row_stats(bf16(masked)[None], 0.6)
+    H2, am2 = sampler.row_stats(bf16(x[keep])[None], 0.6)
+    assert abs(H1[0] - H2[0]) < 1e-12
+    assert np.flatnonzero(keep)[am2[0]] == am1[0]
