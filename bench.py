@@ -12,7 +12,8 @@ and max not counted).  The roofline object is for the dominant kernel (the
 split-key canvas attention kernel), timed with HIP events that the library
 records on its launch stream.  cpu_baseline times the CPU fp64 oracle on a
 bounded sample of the same workload.  The default (bf16) line also carries the
-fp8 canvas step's kernel time and its fraction of the fp8 MFMA peak.
+fp8 canvas step's kernel time and its fraction of the fp8 MFMA peak, and the
+canvas sampler's time per call over one step's logits (--sampler: only that).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--dtype fp8]
 """
@@ -38,8 +39,14 @@ ELEM_BYTES = {"bf16": 2, "fp8": 1}
 
 # the canvas attention kernel of each format, as rocprofv3 names it, and the
 # profile files of its counter summaries
-ATTN_KERNELS = {"bf16": "attn_bf16_kernel<128, false", "fp8": "attn_fp8_kernel<128, false"}
-PROFILE_TAG = {"bf16": "canvas_attn_l8k", "fp8": "canvas_attn_fp8_l8k"}
+ATTN_KERNELS = {"bf16": "attn_bf16_kernel<128, false", "fp8": "attn_fp8_kernel<128, false",
+                "sampler": "row_stats_kernel"}
+PROFILE_TAG = {"bf16": "canvas_attn_l8k", "fp8": "canvas_attn_fp8_l8k", "sampler": "canvas_sample_v262k"}
+PROFILE_WHAT = {"bf16": "the canvas attention kernel (bf16; canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)",
+                "fp8": "the canvas attention kernel (fp8; canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)",
+                "sampler": "the sampler's row statistics kernel (B=1, 256 positions, V=262144 bf16 logits)"}
+PROFILE_RUN = {"bf16": "--steps 2 --warmup 1 --profile-steps", "fp8": "--steps 2 --warmup 1 --profile-steps --dtype fp8",
+               "sampler": "--sampler --steps 10"}
 MOPS_COUNTER = {"bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "fp8": "SQ_INSTS_VALU_MFMA_MOPS_F8"}
 
 
@@ -53,11 +60,13 @@ def traffic_file(dtype):
 # source; it is reported only while the source still matches.
 KERNEL_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
                   for f in ("dg_attn_mfma.hip", "dg_internal.h")]
+SAMPLER_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
+                   for f in ("dg_sample.hip", "dg_internal.h")]
 
 
-def kernel_source_hash():
+def kernel_source_hash(dtype="bf16"):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in SAMPLER_SOURCES if dtype == "sampler" else KERNEL_SOURCES:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -114,7 +123,7 @@ def _counter_per_dispatch(folder, counter, name_part):
 
 def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, dtype="bf16"):
     ATTN_KERNEL = ATTN_KERNELS[dtype]
-    flag = "" if dtype == "bf16" else f" --dtype {dtype}"
+    flag = {"bf16": "", "fp8": " --dtype fp8", "sampler": " --sampler"}[dtype]
     copy_bytes = int(copy_mib) * (1 << 20)
     f_kib, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", ATTN_KERNEL)
     w_kib, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", ATTN_KERNEL)
@@ -125,16 +134,15 @@ def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, d
     fetch = f_kib * 1024.0 * f_scale
     write = w_kib * 1024.0 * w_scale
     lines = [
-        f"# HBM traffic of the canvas attention kernel ({dtype}; canvas step, L=8192, B=1, Hq=16, "
-        "Hkv=8, D=128)",
+        f"# HBM traffic of {PROFILE_WHAT[dtype]}",
         "# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of",
-        f"#   python3 bench.py --steps 2 --warmup 1 --profile-steps{flag}",
+        f"#   python3 bench.py {PROFILE_RUN[dtype]}",
         "# calibrated with the same counters on a plain device-to-device copy of known size",
         f"#   python3 bench.py --copy-probe {copy_mib}",
         "# (each scale = copy bytes / counter bytes of that copy); written by",
         f"#   python3 bench.py --summarize-counters FETCH WRITE COPY_FETCH COPY_WRITE MIB{flag}",
         f"kernel: {ATTN_KERNEL}...>",
-        f"kernel_source_hash: {kernel_source_hash()}",
+        f"kernel_source_hash: {kernel_source_hash(dtype)}",
         f"dispatches_fetch: {nf}",
         f"dispatches_write: {nw}",
         f"fetch_kib_per_dispatch: {f_kib:.1f}",
@@ -206,16 +214,17 @@ def summarize_mfma(pass1_dir, pass2_dir, trace_txt, dtype="bf16"):
     print(open(out).read())
 
 
-def summarize_trace(stats_csv, out_txt, dtype="bf16"):
+def summarize_trace(stats_csv, out_txt, dtype="bf16", sampler=False):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     keep = [r for r in rows if "dg::" in r["Name"] or "copyBuffer" in r["Name"]]
     flag = "" if dtype == "bf16" else f" --dtype {dtype}"
+    run = "--sampler --steps 50" if sampler else f"--steps 10 --warmup 2 --no-cpu-baseline{flag}"
     lines = ["# rocprofv3 --kernel-trace --stats summary (kernels of this library)",
              "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-             f"-d <dir> -o run -- python3 <repo>/bench.py --steps 10 --warmup 2 --no-cpu-baseline{flag}",
+             f"-d <dir> -o run -- python3 <repo>/bench.py {run}",
              "# (written by: python3 bench.py --summarize-trace <dir>/run_kernel_stats.csv OUT"
-             f"{flag})",
+             f"{' --sampler' if sampler else flag})",
              f"{'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_pct':>9}  kernel"]
     for r in keep:
         lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.3f} "
@@ -409,6 +418,38 @@ def fp8_summary(reps=100):
             "kernel": "attn_fp8_kernel<128,false>", "timing": f"median of {reps} calls, warm"}
 
 
+def measure_sampler(reps=50, batch=1):
+    """The canvas sampler (dg_canvas_sample) on one step's logits: B canvases of
+    256 positions over the 262144-token vocabulary, tau 0.8 (the start of the
+    annealing), budget 0.1, stop threshold 0.005.  Median per call over `reps`
+    calls (both launches, torch events on the launch stream); the logits (bf16)
+    are the algorithmic bytes."""
+    import torch
+    import canvas_attention_amd.dg as dg
+    from canvas_attention_amd import synth
+    lg = torch.from_numpy(synth.sampler_logits(1006, batch).view(np.int16)).view(torch.bfloat16).cuda()
+    nz = torch.from_numpy(synth.noise_tokens(1006, batch)).cuda()
+    for _ in range(5):
+        dg.canvas_sample(lg, nz, None, 0.8, 0.1, 0.005)
+    torch.cuda.synchronize()
+    ts = []
+    stream = torch.cuda.current_stream()
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dg.canvas_sample(lg, nz, None, 0.8, 0.1, 0.005)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    us = float(np.median(ts)) * 1e3
+    nbytes = batch * 256 * synth.VOCAB * 2
+    return {"batch": batch, "vocab": synth.VOCAB, "call_us_median": round(us, 3),
+            "logits_bytes": nbytes, "call_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "call_hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "kernels": "row_stats_kernel + select_kernel", "timing": f"median of {reps} calls"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -417,6 +458,8 @@ def main():
     ap.add_argument("--dtype", choices=("bf16", "fp8"), default="bf16",
                     help="storage format of q, K and V (fp8: OCP e4m3, tensor scales 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sampler", action="store_true",
+                    help="only time the canvas sampler (256 x 262144 bf16 logits per canvas)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--profile-steps", action="store_true",
@@ -432,10 +475,10 @@ def main():
                     help="write a kernel summary from a rocprofv3 --stats kernel_stats.csv")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, dtype=args.dtype)
+        summarize_counters(*args.summarize_counters, dtype="sampler" if args.sampler else args.dtype)
         return
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace, dtype=args.dtype)
+        summarize_trace(*args.summarize_trace, dtype=args.dtype, sampler=args.sampler)
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, dtype=args.dtype)
@@ -452,6 +495,9 @@ def main():
         return
 
     torch.cuda.set_device(0)
+    if args.sampler:
+        print(json.dumps({"sampler": measure_sampler(max(args.steps, 10))}), flush=True)
+        return
     m = measure(args.dtype, args.steps, args.warmup, args.profile_steps)
     if args.profile_steps:
         print(json.dumps(m), flush=True)
@@ -475,6 +521,7 @@ def main():
     }
     if args.dtype == "bf16":
         result["fp8"] = fp8_summary()
+        result["sampler"] = measure_sampler()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline("cycle_l8k", args.cpu_seconds, args.dtype)
     print(json.dumps(result), flush=True)
