@@ -7,7 +7,7 @@ and the CPU oracle consume exactly the arrays produced here.
 Recipe (the same for every workload):
   * generator: ``numpy.random.default_rng([seed, tensor_id, seq, block, step])``
     with one seed per workload and tensor ids 0/1 cache K/V, 2/3/4 canvas Q/K/V,
-    5/6/7 commit (block) Q/K/V;
+    5/6/7 commit (block) Q/K/V, 11/12/13 decode Q/K/V;
   * values: ``standard_normal`` drawn in float32, stored as bf16 by rounding to
     nearest-even (fp32 workloads keep the float32 values; fp8 workloads store
     OCP e4m3 bytes, rounded to nearest-even, with tensor scales of 1);
@@ -28,6 +28,7 @@ N_CANVAS = 256
 
 T_CACHE_K, T_CACHE_V, T_Q, T_K, T_V, T_QB, T_KB, T_VB = range(8)
 T_LOGITS, T_NOISE, T_PEAK = 8, 9, 10   # canvas sampler inputs
+T_QD, T_KD, T_VD = 11, 12, 13          # decode Q/K/V of the new tokens
 
 VOCAB = 262144  # vocabulary of the sampled model family ("262k vocabulary")
 
@@ -153,6 +154,16 @@ def block(seed: int, batch: int, hq: int, hkv: int, d: int, dtype: str, block: i
     q = batched(seed, T_QB, batch, N_CANVAS, hq, d, dtype, block)
     k = batched(seed, T_KB, batch, N_CANVAS, hkv, d, dtype, block)
     v = batched(seed, T_VB, batch, N_CANVAS, hkv, d, dtype, block)
+    return q, k, v
+
+
+def decode(seed: int, batch: int, n_new: int, hq: int, hkv: int, d: int, dtype: str,
+           step: int = 0):
+    """Decode inputs of n_new tokens per sequence: Q [B,n_new,Hq,D] and K, V
+    [B,n_new,Hkv,D]; `step` numbers successive decode calls."""
+    q = batched(seed, T_QD, batch, n_new, hq, d, dtype, 0, step)
+    k = batched(seed, T_KD, batch, n_new, hkv, d, dtype, 0, step)
+    v = batched(seed, T_VD, batch, n_new, hkv, d, dtype, 0, step)
     return q, k, v
 
 

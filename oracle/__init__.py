@@ -132,6 +132,19 @@ def commit_attn(q_blk, k_cache, v_cache, prefix_len, k_blk, v_blk, scale=None, r
                  scale, rows, tensor_scales)
 
 
+
+def decode_attn(q, k_cache, v_cache, prefix_len, k_new, v_new, scale=None, rows=None,
+                tensor_scales=None):
+    """AR-mode decode of k new tokens per sequence ("DiffusionGemma Technical
+    Report", paperfeed.app summary, section "The numbers, honestly": the same
+    weights decode causally over the same cache; several drafted tokens at once
+    for hybrid decoding): new token i attends to cache rows 0..L-1 and new rows
+    0..i.  That is the commit's causal rule with k rows in place of 256, so this
+    runs the same fp64 definition with Nc = k = q.shape[1].  The cache append
+    that follows is append_block with the k new rows."""
+    return _attn("dgo_commit_attn", q, k_cache, v_cache, prefix_len, k_new, v_new,
+                 scale, rows, tensor_scales)
+
 def append_block(k_blk, v_blk, k_cache, v_cache, prefix_len):
     """Copy block K/V rows into cache rows L_b..L_b+Nc-1 in place (bitwise)."""
     lib = _load()
