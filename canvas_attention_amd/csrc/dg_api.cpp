@@ -3,7 +3,9 @@
 // Entry points follow the two attention modes of "DiffusionGemma Technical
 // Report" (paperfeed.app summary, section "The mechanism: an AR model turned
 // inside out"): the bidirectional canvas step over [cache ; canvas] and the
-// causal block commit that appends the block to the cache.
+// causal block commit that appends the block to the cache; and the AR mode of
+// the same weights (section "The numbers, honestly"): causal decoding of 1..16
+// new tokens over the same cache.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdarg.h>
@@ -79,14 +81,22 @@ int rows_per_unit(int dtype, int variant) {
   return dtype == DG_BF16 ? dg::variant_rows(variant) : dg::kRowsF32;
 }
 
-dg_status check_shape(const dg_shape* s) {
+// Call kinds: the canvas step, the block commit and decode attention.
+enum Mode { kCanvasStep = 0, kCommit = 1, kDecode = 2 };
+
+dg_status check_shape(const dg_shape* s, Mode mode = kCanvasStep) {
   if (!s) return fail(DG_ERR_NULL, "shape is NULL");
   if (s->dtype != DG_BF16 && s->dtype != DG_F32 && s->dtype != DG_FP8)
     return fail(DG_ERR_DTYPE, "unknown dtype %d (DG_BF16=0, DG_F32=1, DG_FP8=2)", s->dtype);
   if (s->batch < 1 || s->batch > DG_MAX_BATCH)
     return fail(DG_ERR_SHAPE, "batch %d outside 1..%d", s->batch, DG_MAX_BATCH);
-  if (s->n_canvas != DG_N_CANVAS)
+  if (mode == kDecode) {
+    if (s->n_canvas < 1 || s->n_canvas > DG_MAX_DECODE)
+      return fail(DG_ERR_SHAPE, "decode of %d new tokens, must be 1..%d", s->n_canvas,
+                  DG_MAX_DECODE);
+  } else if (s->n_canvas != DG_N_CANVAS) {
     return fail(DG_ERR_SHAPE, "n_canvas %d, must be %d", s->n_canvas, DG_N_CANVAS);
+  }
   if (s->n_heads_kv < 1 || s->n_heads_q < 1 || s->n_heads_q > 1024)
     return fail(DG_ERR_SHAPE, "head counts Hq=%d Hkv=%d invalid", s->n_heads_q, s->n_heads_kv);
   if (s->n_heads_q % s->n_heads_kv != 0)
@@ -147,6 +157,8 @@ void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
   if (forced) kappa = forced;
   memset(p, 0, sizeof *p);
   p->batch = s->batch;
+  p->n_q = dg::kCanvas;
+  p->rcp_m = dg::rcp_u32((uint32_t)(dg::kCanvas * G));
   p->variant = variant;
   p->n_rowtiles = NRT;
   p->rows_per_unit = R;
@@ -169,6 +181,65 @@ void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
     units += S * per_split;
   }
   p->n_units = units;
+}
+
+// Decode plan: tiles of R packed rows (32 on the matrix cores, 64 for fp32), and
+// key splits sized so that the units fill the device once.  With P = B*Hkv*NRT
+// units per split index, splits of kappa >= W / (T - P) keys give at most
+// W/kappa + P <= T units (each sequence adds at most one partial split per head
+// and tile), so no second round of workgroups waits behind the first.
+int decode_rows(int dtype) { return mfma_path(dtype) ? dg::kDecodeRows : dg::kRowsF32; }
+
+int decode_target_units(int dtype) {
+  // the matrix-core decode kernel takes one workgroup per CU (its LDS rings); the
+  // fp32 kernel runs one wave per unit, four per CU
+  return device_cu_count() * (mfma_path(dtype) ? 1 : 4);
+}
+
+void make_decode_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
+  const int nq = s->n_canvas;
+  const int R = decode_rows(s->dtype);
+  const int G = s->n_heads_q / s->n_heads_kv;
+  const int NRT = (nq * G + R - 1) / R;
+  const int per_split = s->n_heads_kv * NRT;
+  int64_t W = 0;
+  for (int b = 0; b < s->batch; b++) W += (int64_t)(prefix_len[b] + nq) * per_split;
+  const int64_t T = decode_target_units(s->dtype);
+  const int64_t P = (int64_t)s->batch * per_split;
+  const int gran = key_granule(s->dtype);
+  const int64_t avail = T > 2 * P ? T - P : T;
+  int64_t kappa = (W + avail - 1) / avail;
+  kappa = ((kappa + gran - 1) / gran) * gran;
+  // at least one chunk per wave of the unit
+  kappa = std::max<int64_t>(kappa, mfma_path(s->dtype) ? (int64_t)dg::kDecodeWaves * gran : 64);
+  const int forced = forced_split_keys(s->dtype);
+  if (forced) kappa = forced;
+  memset(p, 0, sizeof *p);
+  p->batch = s->batch;
+  p->n_q = nq;
+  p->rcp_m = dg::rcp_u32((uint32_t)(nq * G));
+  p->variant = dg::kDefaultVariant;
+  p->n_rowtiles = NRT;
+  p->rows_per_unit = R;
+  p->g = G;
+  p->rcp_g = dg::rcp_u32((uint32_t)G);
+  p->rcp_nrt = dg::rcp_u32((uint32_t)NRT);
+  int64_t units = 0;
+  for (int b = 0; b < s->batch; b++) {
+    const int64_t K = (int64_t)prefix_len[b] + nq;
+    int64_t S = (K + kappa - 1) / kappa;
+    int64_t sk = (K + S - 1) / S;
+    sk = ((sk + gran - 1) / gran) * gran;
+    S = (K + sk - 1) / sk;
+    p->seq[b].prefix_len = prefix_len[b];
+    p->seq[b].n_splits = (int)S;
+    p->seq[b].split_keys = (int)sk;
+    p->seq[b].unit_base = (int)std::min<int64_t>(units, INT32_MAX);
+    p->seq[b].rcp_s = dg::rcp_u32((uint32_t)S);
+    p->seq[b].rcp_snrt = dg::rcp_u32((uint32_t)(S * NRT));
+    units += S * per_split;
+  }
+  p->n_units = (int)std::min<int64_t>(units, INT32_MAX);
 }
 
 // Bytes of one partial row: the normalised output (bf16 or fp32) plus max and sum.
@@ -218,19 +289,22 @@ struct Call {
   Plan plan;
   AttnArgs args;
   bool causal;
+  Mode mode;
 };
 
 dg_status prepare(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
                   const int32_t* prefix_len, const dg_kv* kv_new, void* out, void* workspace,
-                  size_t ws_bytes, bool commit, Call* c) {
-  dg_status st = check_shape(shape);
+                  size_t ws_bytes, Mode mode, Call* c) {
+  dg_status st = check_shape(shape, mode);
   if (st) return st;
+  const bool commit = mode != kCanvasStep;  // causal, and the new rows join the cache
+  const int nq = mode == kDecode ? shape->n_canvas : DG_N_CANVAS;
   if (!q || !out || !kv_cache || !kv_new || !prefix_len)
     return fail(DG_ERR_NULL, "a required argument is NULL (q, out, caches or prefix_len)");
-  if (!kv_new->k || !kv_new->v) return fail(DG_ERR_NULL, "canvas/block K or V is NULL");
-  if (kv_new->capacity != DG_N_CANVAS)
-    return fail(DG_ERR_SHAPE, "canvas/block capacity %lld, must be %d",
-                (long long)kv_new->capacity, DG_N_CANVAS);
+  if (!kv_new->k || !kv_new->v) return fail(DG_ERR_NULL, "canvas/block/new K or V is NULL");
+  if (kv_new->capacity != nq)
+    return fail(DG_ERR_SHAPE, "canvas/block/new K/V capacity %lld, must be %d",
+                (long long)kv_new->capacity, nq);
   if (kv_cache->capacity < 0) return fail(DG_ERR_CAPACITY, "negative cache capacity");
   if ((!kv_cache->k || !kv_cache->v) && (kv_cache->capacity > 0 || commit))
     return fail(DG_ERR_NULL, "cache K or V is NULL");
@@ -240,16 +314,21 @@ dg_status prepare(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
   for (int b = 0; b < shape->batch; b++) {
     const int64_t L = prefix_len[b];
     if (L < 0) return fail(DG_ERR_CAPACITY, "prefix_len[%d] = %lld is negative", b, (long long)L);
-    const int64_t need = commit ? L + DG_N_CANVAS : L;
+    const int64_t need = commit ? L + nq : L;
     if (need > kv_cache->capacity)
       return fail(DG_ERR_CAPACITY, "prefix_len[%d] = %lld%s exceeds cache capacity %lld", b,
-                  (long long)L, commit ? " + 256" : "", (long long)kv_cache->capacity);
+                  (long long)L, commit ? (mode == kDecode ? " + new tokens" : " + 256") : "",
+                  (long long)kv_cache->capacity);
     if (L + DG_N_CANVAS > INT32_MAX / 2)
       return fail(DG_ERR_CAPACITY, "prefix_len[%d] too large", b);
   }
   c->shape = *shape;
   c->causal = commit;
-  make_plan(shape, prefix_len, &c->plan);
+  c->mode = mode;
+  if (mode == kDecode)
+    make_decode_plan(shape, prefix_len, &c->plan);
+  else
+    make_plan(shape, prefix_len, &c->plan);
   // unit and row indices stay below 2^16, which keeps every kernel division n/d with
   // n*d < 2^32 (the reciprocal-multiplier form is exact there)
   if (c->plan.n_units >= dg::kMaxUnits)
@@ -288,9 +367,15 @@ dg_status launch(const Call& c, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int dt = c.shape.dtype;
   time_begin(0, st);
-  int err = dt == DG_BF16  ? dg::launch_attn_bf16(c.args, c.plan, c.shape.head_dim, c.causal, stream)
-            : dt == DG_FP8 ? dg::launch_attn_fp8(c.args, c.plan, c.causal, stream)
-                           : dg::launch_attn_f32(c.args, c.plan, c.shape.head_dim, c.causal, stream);
+  int err;
+  if (c.mode == kDecode && mfma_path(dt))
+    err = dg::launch_decode(c.args, c.plan, dt, c.shape.head_dim, stream);
+  else if (dt == DG_BF16)
+    err = dg::launch_attn_bf16(c.args, c.plan, c.shape.head_dim, c.causal, stream);
+  else if (dt == DG_FP8)
+    err = dg::launch_attn_fp8(c.args, c.plan, c.causal, stream);
+  else
+    err = dg::launch_attn_f32(c.args, c.plan, c.shape.head_dim, c.causal, stream);
   time_end(0, st);
   if (err != 0)
     return fail(DG_ERR_HIP, "attention kernel launch failed: %s",
@@ -305,7 +390,8 @@ dg_status launch(const Call& c, void* stream) {
       return fail(DG_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString((hipError_t)err));
   }
   if (getenv("DG_LOG")) {
-    fprintf(stderr, "[dg] %s dtype=%d variant=%d units=%d R=%d NRT=%d", c.causal ? "commit" : "canvas",
+    static const char* const kModeName[] = {"canvas", "commit", "decode"};
+    fprintf(stderr, "[dg] %s dtype=%d variant=%d units=%d R=%d NRT=%d", kModeName[c.mode],
             dt, c.plan.variant, c.plan.n_units, c.plan.rows_per_unit, c.plan.n_rowtiles);
     for (int b = 0; b < c.plan.batch; b++)
       fprintf(stderr, " | b%d L=%d S=%d keys/split=%d", b, c.plan.seq[b].prefix_len,
@@ -341,7 +427,7 @@ dg_status dg_canvas_attn(const dg_shape* shape, const void* q, const dg_kv* kv_c
                          void* workspace, size_t ws_bytes, void* stream) {
   Call c;
   dg_status st = prepare(shape, q, kv_cache, prefix_len, kv_canvas, out, workspace, ws_bytes,
-                         false, &c);
+                         kCanvasStep, &c);
   if (st) return st;
   return launch(c, stream);
 }
@@ -351,7 +437,34 @@ dg_status dg_commit_block(const dg_shape* shape, const void* q_blk, const dg_kv*
                           void* workspace, size_t ws_bytes, void* stream) {
   Call c;
   dg_status st = prepare(shape, q_blk, kv_cache, prefix_len, kv_blk, out, workspace, ws_bytes,
-                         true, &c);
+                         kCommit, &c);
+  if (st) return st;
+  return launch(c, stream);
+}
+
+size_t dg_decode_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len) {
+  if (check_shape(shape, kDecode) != DG_OK || max_prefix_len < 0 ||
+      max_prefix_len > INT32_MAX / 2)
+    return 0;
+  // the decode plan never exceeds T + B*Hkv*NRT units (see make_decode_plan)
+  const int nq = shape->n_canvas, R = decode_rows(shape->dtype);
+  const int G = shape->n_heads_q / shape->n_heads_kv;
+  const int64_t per_split = (int64_t)shape->n_heads_kv * ((nq * G + R - 1) / R);
+  int64_t units = decode_target_units(shape->dtype) + (int64_t)shape->batch * per_split;
+  const int forced = forced_split_keys(shape->dtype);
+  if (forced) {
+    const int64_t S = (max_prefix_len + nq + forced - 1) / forced;
+    units = std::max<int64_t>(units, S * shape->batch * per_split);
+  }
+  return (size_t)units * R * partial_row_bytes(shape);
+}
+
+dg_status dg_decode_attn(const dg_shape* shape, const void* q, const dg_kv* kv_new,
+                         const dg_kv* kv_cache, const int32_t* prefix_len, void* out,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  Call c;
+  dg_status st = prepare(shape, q, kv_cache, prefix_len, kv_new, out, workspace, ws_bytes,
+                         kDecode, &c);
   if (st) return st;
   return launch(c, stream);
 }
@@ -364,7 +477,7 @@ dg_status dg_canvas_step_loop(const dg_shape* shape, int32_t n_steps, const void
   if (n_steps < 0) return fail(DG_ERR_SHAPE, "n_steps %d is negative", n_steps);
   Call c;
   dg_status st = prepare(shape, q, kv_cache, prefix_len, kv_canvas, out, workspace, ws_bytes,
-                         false, &c);
+                         kCanvasStep, &c);
   if (st) return st;
   const size_t es = elem_size(shape->dtype), eo = out_elem_size(shape->dtype);
   if (((q_step_stride * (int64_t)es) & 15) || ((kv_step_stride * (int64_t)es) & 15) ||

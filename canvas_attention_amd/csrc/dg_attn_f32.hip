@@ -4,7 +4,8 @@
 // (canvas step: unmasked attention over [cache ; canvas]; commit: block row i
 // sees block keys 0..i and the block K/V are appended to the cache --
 // "DiffusionGemma Technical Report", paperfeed.app summary, section "The
-// mechanism: an AR model turned inside out").  Products and sums are true fp32
+// mechanism: an AR model turned inside out"; decode: the commit's rule for the
+// 1..16 new tokens of the same section's AR mode, "AR mode survives").  Products and sums are true fp32
 // FMAs on the vector ALU: this path exists for exact-precision checking, not
 // speed.  One wave64 per unit, one packed query row per lane; 32-key K/V tiles
 // are staged in LDS and read as broadcasts.  Per tile the exact tile max is
@@ -41,7 +42,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, Plan plan) {
   const int L = sp.prefix_len;
   const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = Hq / Hkv;
   const int row0 = rt * R;
-  int kend = L + kCanvas;
+  const int NQ = plan.n_q, M = NQ * G;  // new rows per head, packed rows per kv head
+  int kend = L + NQ;
   if (CAUSAL) kend = min(kend, L + (row0 + R - 1) / G + 1);
   const int kbeg = s * sp.split_keys;
   const int kstop = min(kbeg + sp.split_keys, kend);
@@ -54,23 +56,26 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, Plan plan) {
   if (CAUSAL && a.k_append != nullptr) {
     const int cnt = sp.n_splits * NRT;
     const int w = s * NRT + rt;
-    const int rpu = (kCanvas + cnt - 1) / cnt;
-    const int r0 = min(kCanvas, w * rpu), r1 = min(kCanvas, r0 + rpu);
+    const int rpu = (NQ + cnt - 1) / cnt;
+    const int r0 = min(NQ, w * rpu), r1 = min(NQ, r0 + rpu);
     const int per = (r1 - r0) * D4;
     for (int idx = lane; idx < 2 * per; idx += 64) {
       const int which = idx / per, rem = idx % per;
       const int r = r0 + rem / D4, c = rem % D4;
-      const int64_t src = ((int64_t)(b * kCanvas + r) * Hkv + g) * D + 4 * c;
+      const int64_t src = ((int64_t)(b * NQ + r) * Hkv + g) * D + 4 * c;
       const int64_t dst = (((int64_t)b * a.cap + L + r) * Hkv + g) * D + 4 * c;
       *(float4*)((float*)(which ? a.v_append : a.k_append) + dst) =
           *(const float4*)((which ? vn : kn) + src);
     }
   }
 
-  const int prow = row0 + lane;
+  // lanes past the last packed row (a decode tile) compute on a copy of that row
+  // and write nothing
+  const int prow = min(row0 + lane, M - 1);
+  const bool valid = row0 + lane < M;
   const int qi = prow / G, hh = prow % G;
   float q[D];
-  const float* qp = (const float*)a.q + ((int64_t)(b * kCanvas + qi) * Hq + g * G + hh) * D;
+  const float* qp = (const float*)a.q + ((int64_t)(b * NQ + qi) * Hq + g * G + hh) * D;
 #pragma unroll
   for (int d = 0; d < D; d++) q[d] = qp[d];
   float o[D];
@@ -90,7 +95,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, Plan plan) {
         kp = kc + off;
         vp = vc + off;
       } else {
-        const int64_t off = ((int64_t)(b * kCanvas + key - L) * Hkv + g) * D;
+        const int64_t off = ((int64_t)(b * NQ + key - L) * Hkv + g) * D;
         kp = kn + off;
         vp = vn + off;
       }
@@ -141,7 +146,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, Plan plan) {
 
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (sp.n_splits == 1) {
-    float* op = (float*)a.out + ((int64_t)(b * kCanvas + qi) * Hq + g * G + hh) * D;
+    if (!valid) return;
+    float* op = (float*)a.out + ((int64_t)(b * NQ + qi) * Hq + g * G + hh) * D;
 #pragma unroll
     for (int c = 0; c < D4; c++)
       *(float4*)(op + 4 * c) =

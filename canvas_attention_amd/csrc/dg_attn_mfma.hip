@@ -1395,6 +1395,305 @@ void attn_rows_kernel(AttnArgs a, Plan plan) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode attention: the AR mode of the same weights and cache, and hybrid
+// decoding that checks several drafted tokens in one pass ("DiffusionGemma
+// Technical Report", paperfeed.app summary, section "The numbers, honestly", the
+// AR-mode and concurrency paragraphs).  n_q = 1..16 new tokens per sequence:
+// token i attends to every cache row and to new rows 0..i (the commit's causal
+// rule), and the new K/V rows are appended to the cache.
+//
+// With a few query rows per kv head every K/V byte feeds at most 32 packed rows:
+// the work is a stream of the cache out of HBM, so the kernel is laid out for
+// bytes in flight rather than for matrix-core issue.
+//   * A unit is one tile of 32 packed rows (the n_q*G rows of a kv head, padded;
+//     more rows make more tiles, which re-read their keys from L2) against one
+//     key split.  A workgroup of NW waves per CU.
+//   * Wave w takes chunks w, w+NW, ... of the split and streams each into its own
+//     ring of NST LDS stages (K tile, then V tile) with global_load_lds_dwordx4:
+//     no workgroup barrier inside the loop, NST-1 chunks of K and V per wave in
+//     flight while it works on one, and every load instruction covers whole
+//     128-byte lines.  The query tile arrives the same way, once, behind one
+//     barrier.
+//   * Per chunk the arithmetic is the canvas kernel's: transposed scores on the
+//     32x32 matrix cores, the lazily rescaled log2-domain softmax, transposing V
+//     reads.  Padding rows compute on a copy of the last row and are not written.
+//   * The waves' states are merged through LDS at the end, and the unit writes
+//     one partial (or the output, when its sequence has a single split).
+//   * The first unit of each (sequence, kv head) copies the new K/V rows into the
+//     cache: loaded at the start, stored at the end, so that the copy never holds
+//     up the stream.  No unit reads cache rows at or past L (new keys come from
+//     the new-row buffers), so the copy races with nothing.
+template <class F, int D, int NW, int NST>
+__global__ __launch_bounds__(64 * NW) void decode_kernel(AttnArgs a, Plan plan) {
+  constexpr bool F8 = is_fp8<F>;
+  constexpr int TK = F::TK, MB = D / 32, ROWB = D * F::ESZ, CH = ROWB / 16;
+  constexpr int TILEB = TK * ROWB;  // bytes of one chunk of K (or V)
+  constexpr int RPI = 1024 / ROWB;  // rows per 1 KB load
+  constexpr int IPT = TILEB / 1024; // loads per tile
+  static_assert(IPT % 4 == 0, "tiles of whole 4 KB load groups");
+  constexpr int NG = IPT / 4;
+  constexpr int PERCH = 2 * IPT;    // loads per chunk (K and V)
+  static_assert(NST >= 2 && NST * PERCH <= 63, "outstanding loads within the vmcnt range");
+  constexpr int SLOTB = 2 * TILEB;  // one stage: K tile, then V tile
+  constexpr int WAVEB = NST * SLOTB;
+  constexpr int QB = kDecodeRows * ROWB;  // the unit's query rows
+  constexpr int QPW = QB / 1024 / NW;     // query loads per wave
+  static_assert(QPW >= 1 && QPW * NW * 1024 == QB, "query loads split over the waves");
+  constexpr int PER = MB * 16 + 4;        // floats per lane of merge state
+  static_assert(64 * PER * 4 <= WAVEB, "a wave's merge state fits in its ring");
+  constexpr int NT = 64 * NW;
+  constexpr int APT = (2 * DG_MAX_DECODE * CH + NT - 1) / NT;  // appended chunks per thread
+  __shared__ __attribute__((aligned(1024))) char lds[NW * WAVEB + QB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int U = xcd_remap(blockIdx.x, gridDim.x);
+  SeqPlan sp;
+  const Unit u = decode_unit(plan, U, sp);
+  const int L = sp.prefix_len, NQ = plan.n_q, G = plan.g, M = NQ * G;
+  const int Hq = a.n_heads_q, Hkv = a.n_heads_kv;
+  const int row0 = u.rt * kDecodeRows;
+  // keys the tile can see: the cache and the new rows up to its last token
+  const int kend = L + min(NQ, div_rcp(min(row0 + kDecodeRows, M) - 1, plan.rcp_g) + 1);
+  const int kbeg = u.s * sp.split_keys;
+  const int kstop = min(kbeg + sp.split_keys, kend);
+  const int ntiles = kstop > kbeg ? (kstop - kbeg + TK - 1) / TK : 0;
+  const int nmine = uniform(ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0);
+
+  const uint32_t rsb = (uint32_t)Hkv * ROWB;  // bytes between rows of one kv head
+  const char* kc = (const char*)a.k_cache + ((int64_t)u.b * a.cap * Hkv + u.g) * ROWB;
+  const char* vc = (const char*)a.v_cache + ((int64_t)u.b * a.cap * Hkv + u.g) * ROWB;
+  const char* kn = (const char*)a.k_new + ((int64_t)u.b * NQ * Hkv + u.g) * ROWB;
+  const char* vn = (const char*)a.v_new + ((int64_t)u.b * NQ * Hkv + u.g) * ROWB;
+
+  // ---- the cache append, first half: load the new rows of head g
+  const bool appender = a.k_append != nullptr && u.s == 0 && u.rt == 0;
+  const int napp = appender ? 2 * NQ * CH : 0;  // 16-byte chunks of K and V
+  uint4 app[APT];
+#pragma unroll
+  for (int r = 0; r < APT; r++) {
+    const int idx = tid + NT * r;
+    if (idx < napp) {
+      const int which = idx >= NQ * CH, rem = idx - which * NQ * CH;
+      app[r] = *(const uint4*)((which ? vn : kn) + (int64_t)(rem / CH) * rsb + 16 * (rem % CH));
+    }
+  }
+
+  const uint32_t lbase = lds_addr(lds);
+  const uint32_t qarea = lbase + NW * WAVEB;
+  const uint32_t wring = lbase + (uint32_t)wave * WAVEB;
+  const int lr = lane / CH, lp = lane % CH;
+  // swizzle of the 16-byte chunks of tile row r (see lane_offsets, lane_offsets8)
+  auto swk = [](int r) { return F8 ? swz8(r) : (r & (CH - 1)); };
+  auto swv = [](int r) { return F8 ? swz8(r) : ((4 * (r & 3)) & (CH - 1)); };
+
+  // ---- the query tile: packed row p = i*G + hh of the tile (clamped to the last
+  //      row) into row p - row0 of the query area, swizzled like a K tile
+  {
+    const char* qb = (const char*)a.q + ((int64_t)u.b * NQ * Hq + u.g * G) * ROWB;
+#pragma unroll
+    for (int e = 0; e < QPW; e++) {
+      const int blk = wave * QPW + e, r = blk * RPI + lr;
+      const int p = min(row0 + r, M - 1), i = div_rcp(p, plan.rcp_g);
+      gll_vaddr(qb + (int64_t)(i * Hq + p - i * G) * ROWB + 16 * (lp ^ swk(r)),
+                uniform(qarea + 1024u * blk));
+    }
+  }
+
+  // ---- chunk loads.  Load e of a tile covers tile rows e*RPI .. e*RPI+RPI-1: lane
+  //      l writes 16 bytes at 16l of that 1 KB block (row l / CH, physical chunk
+  //      l % CH) and fetches the logical chunk the swizzle stores there.  A chunk
+  //      wholly inside the cache is issued as scalar base + lane offsets (offsets
+  //      less the 1 KB instruction offsets); a chunk reaching the new rows or the
+  //      end of the split forms its rows per lane (rows past the end clamped onto
+  //      the last key: loaded, then masked).
+  uint32_t kvo[IPT], vvo[IPT];
+#pragma unroll
+  for (int e = 0; e < IPT; e++) {
+    const int r = e * RPI + lr;
+    kvo[e] = (uint32_t)r * rsb + 16u * (uint32_t)(lp ^ swk(r)) - 1024u * (uint32_t)(e % 4);
+    vvo[e] = (uint32_t)r * rsb + 16u * (uint32_t)(lp ^ swv(r)) - 1024u * (uint32_t)(e % 4);
+  }
+  const int kclear = min(L, kstop);  // chunks ending at or below this key need no mask
+  auto issue_chunk = [&](int c, uint32_t slot) {
+    const int key0 = kbeg + (c * NW + wave) * TK;
+    if (key0 + TK <= kclear) {
+      const char* kb = uniform_ptr(kc + (int64_t)key0 * rsb);
+      const char* vb = uniform_ptr(vc + (int64_t)key0 * rsb);
+#pragma unroll
+      for (int gi = 0; gi < NG; gi++) {
+        gll_block<4>(kb, kvo + 4 * gi, uniform(slot + 4096u * gi));
+        gll_block<4>(vb, vvo + 4 * gi, uniform(slot + TILEB + 4096u * gi));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < IPT; e++) {
+        const int r = e * RPI + lr, key = min(key0 + r, kstop - 1);
+        const int64_t ro = key < L ? (int64_t)key * rsb : (int64_t)(key - L) * rsb;
+        gll_vaddr((key < L ? kc : kn) + ro + 16 * (lp ^ swk(r)), uniform(slot + 1024u * e));
+        gll_vaddr((key < L ? vc : vn) + ro + 16 * (lp ^ swv(r)), uniform(slot + TILEB + 1024u * e));
+      }
+    }
+  };
+
+  const auto lo = [&] {
+    if constexpr (F8) return lane_offsets8(lane);
+    else return lane_offsets<D>(lane);
+  }();
+  using Ops = typename std::conditional<F8, Ops8, Ops16<D>>::type;
+  using KAddr = typename std::conditional<F8, uint32_t[2][2], uint32_t[D / 16]>::type;
+  KAddr kaddr;
+  uint32_t vaddr[MB];
+  Ops op;
+  if constexpr (F8) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) op.ones[i] = 0x38383838;  // e4m3 1.0 in every byte
+#pragma unroll
+    for (int i = 0; i < 16; i++) op.rs[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+      for (int part = 0; part < 2; part++) kaddr[ks][part] = wring + lo.k[ks][part];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ks++) kaddr[ks] = wring + lo.k[ks];
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++) vaddr[mb] = wring + TILEB + lo.v[mb];
+
+  // ---- prologue: the first NST chunks of this wave, then the query tile
+#pragma unroll
+  for (int c = 0; c < NST; c++)
+    if (c < nmine) issue_chunk(c, wring + c * SLOTB);
+  if (nmine >= NST)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NST * PERCH) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (F8) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) op.q[ks] = lds_read_2x16(qarea + lo.q[ks][0], qarea + lo.q[ks][1]);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ks++) op.q[ks] = *(const LDS_AS bf16x8*)(uintptr_t)(qarea + lo.k[ks]);
+  }
+
+  const float c2 = a.scale_log2;
+  const int qi = div_rcp(min(row0 + n, M - 1), plan.rcp_g);  // token of this lane's row
+  State<MB> acc;
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc.o[mb][i] = 0.f;
+  acc.mlog = -1e30f;
+  acc.lsum = 0.f;
+  acc.thr = (acc.mlog + (F::kBias + F::kThreshold)) / c2;
+
+  // ---- the stream: chunk c of this wave in stage c mod NST; the stage is refilled
+  //      with chunk c+NST once the operand reads of chunk c have returned
+  for (int c0 = 0; c0 < nmine; c0 += NST) {
+#pragma unroll
+    for (int j = 0; j < NST; j++) {
+      const int c = c0 + j;
+      if (c >= nmine) break;
+      if (c + NST <= nmine)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 1) * PERCH) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const uint32_t off = (uint32_t)j * SLOTB;
+      const int key0 = kbeg + (c * NW + wave) * TK;
+      load_k_operands(kaddr, off, op);
+      scores(op);
+      load_v_operands(vaddr, off, op);
+      prepare_scores<MB, true>(op, key0 + TK > kclear, key0, kstop, L, qi, h, c2, acc);
+      numerators<MB>(op, c2, acc);
+      values<MB>(op, acc);
+      if (c + NST < nmine) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue_chunk(c + NST, wring + off);
+      }
+    }
+  }
+  if constexpr (F8) acc.lsum = h == 0 ? op.rs[0] : 0.f;
+
+  // ---- the cache append, second half
+#pragma unroll
+  for (int r = 0; r < APT; r++) {
+    const int idx = tid + NT * r;
+    if (idx < napp) {
+      const int which = idx >= NQ * CH, rem = idx - which * NQ * CH;
+      const int64_t dst = ((int64_t)u.b * a.cap * Hkv + u.g) * ROWB + (int64_t)(L + rem / CH) * rsb + 16 * (rem % CH);
+      *(uint4*)((char*)(which ? a.v_append : a.k_append) + dst) = app[r];
+    }
+  }
+
+  // ---- merge the waves: waves 1.. leave their state in their own ring (all of
+  //      their loads and reads are complete), wave 0 folds it in
+  if (wave > 0) {
+    float4* dst = (float4*)(lds + wave * WAVEB) + lane * (PER / 4);
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        dst[mb * 4 + i] = make_float4(acc.o[mb][4 * i], acc.o[mb][4 * i + 1], acc.o[mb][4 * i + 2],
+                                      acc.o[mb][4 * i + 3]);
+    dst[MB * 4] = make_float4(acc.mlog, acc.lsum, 0.f, 0.f);
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 1; w < NW; w++) {
+    const float4* src = (const float4*)(lds + w * WAVEB) + lane * (PER / 4);
+    const float4 ml = src[MB * 4];
+    const float mn = fmaxf(acc.mlog, ml.x);
+    const float a1 = __builtin_amdgcn_exp2f(acc.mlog - mn);
+    const float a2 = __builtin_amdgcn_exp2f(ml.x - mn);
+    acc.mlog = mn;
+    acc.lsum = acc.lsum * a1 + ml.y * a2;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float4 v = src[mb * 4 + i];
+        acc.o[mb][4 * i] = acc.o[mb][4 * i] * a1 + v.x * a2;
+        acc.o[mb][4 * i + 1] = acc.o[mb][4 * i + 1] * a1 + v.y * a2;
+        acc.o[mb][4 * i + 2] = acc.o[mb][4 * i + 2] * a1 + v.z * a2;
+        acc.o[mb][4 * i + 3] = acc.o[mb][4 * i + 3] * a1 + v.w * a2;
+      }
+  }
+
+  // ---- the tile's rows: normalised, rounded to bf16; lane (n, h) holds head_dim
+  //      32mb + 8q + 4h .. +3 of row n for every (mb, q)
+  const float lt = partner_sum(acc.lsum);
+  const float inv = lt > 0.f ? (F8 ? a.out_scale : 1.f) / lt : 0.f;
+  const int p = row0 + n;
+  if (p >= M) return;
+  const bool direct = sp.n_splits == 1;
+  const int i = div_rcp(p, plan.rcp_g);
+  uint16_t* dst = direct ? (uint16_t*)a.out + ((int64_t)(u.b * NQ + i) * Hq + u.g * G + p - i * G) * D
+                         : (uint16_t*)a.part_o + ((int64_t)U * kDecodeRows + n) * D;
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4e;
+      bf16x4e v;
+#pragma unroll
+      for (int j = 0; j < 4; j++) v[j] = (__bf16)(acc.o[mb][4 * q4 + j] * inv);
+      *(bf16x4e*)(dst + 32 * mb + 8 * q4 + 4 * h) = v;
+    }
+  if (!direct && h == 0)
+    *(float2*)(a.part_ml + ((int64_t)U * kDecodeRows + n) * 2) = make_float2(acc.mlog, lt);
+}
+
+template <class F, int D, int NST>
+int launch_decode_t(const AttnArgs& a, const Plan& p, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<F, D, kDecodeWaves, NST>), dim3(p.n_units), dim3(64 * kDecodeWaves),
+                     0, st, a, p);
+  return (int)hipGetLastError();
+}
+
 template <int D, bool CAUSAL, int WM, int WK, int NSLOT>
 int launch_one(const AttnArgs& a, const Plan& p, hipStream_t st) {
   hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, WM, WK, NSLOT>), dim3(p.n_units), dim3(512), 0,
@@ -1427,6 +1726,14 @@ int launch_fp8(const AttnArgs& a, const Plan& p, hipStream_t st) {
 int launch_attn_fp8(const AttnArgs& a, const Plan& p, bool causal, void* stream) {
   if (p.n_units == 0) return 0;
   return causal ? launch_fp8<true>(a, p, (hipStream_t)stream) : launch_fp8<false>(a, p, (hipStream_t)stream);
+}
+
+int launch_decode(const AttnArgs& a, const Plan& p, int dtype, int head_dim, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (p.n_units == 0) return 0;
+  if (dtype == DG_FP8) return launch_decode_t<FmtFp8, 128, 2>(a, p, st);
+  if (head_dim == 128) return launch_decode_t<FmtBf16, 128, 2>(a, p, st);
+  return launch_decode_t<FmtBf16, 64, 4>(a, p, st);
 }
 
 int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream) {

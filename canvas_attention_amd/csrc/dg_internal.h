@@ -1,10 +1,11 @@
 // dg_internal.h -- types shared by the host API and the gfx950 kernels of libdg.
 //
 // Work decomposition ("split-key plan").  For every sequence b the key space
-// of one call is the concatenation [cache rows 0..L_b-1 ; canvas or block rows
-// 0..255].  Query rows of one kv head are packed: packed row p = i*G + hh is
-// canvas row i of query head g*G + hh, so the G query heads sharing kv head g
-// form one matrix of 256*G rows.  A work unit is (sequence b, kv head g, key
+// of one call is the concatenation [cache rows 0..L_b-1 ; new rows 0..n_q-1]
+// (the canvas or block of 256 rows, or the 1..16 tokens of a decode call).
+// Query rows of one kv head are packed: packed row p = i*G + hh is new row i of
+// query head g*G + hh, so the G query heads sharing kv head g form one matrix of
+// n_q*G rows.  A work unit is (sequence b, kv head g, key
 // split s, row tile rt): rows [rt*R, rt*R+R) of that packed matrix against keys
 // [s*split_keys, min((s+1)*split_keys, end)).  Each unit writes one partial
 // result (normalised output rows plus log2-domain max and sum) that a merge
@@ -45,9 +46,12 @@ inline int variant_rows(int v) { return v == kVariantR128 ? 128 : 256; }
 
 struct Plan {
   int32_t batch;
+  int32_t n_q;          // query rows per sequence and head: 256 (canvas, commit) or the
+                        // decode call's new tokens (1..DG_MAX_DECODE)
+  uint32_t rcp_m;       // div_rcp multiplier of n_q * G (packed rows per kv head)
   int32_t variant;      // bf16 kernel shape (kVariant*); rows_per_unit follows from it
   int32_t n_units;      // total logical units = grid size of the attention kernel (< 2^16)
-  int32_t n_rowtiles;   // NRT = 256*G / R
+  int32_t n_rowtiles;   // NRT = ceil(n_q*G / R)
   int32_t rows_per_unit;// R
   int32_t g;            // G = query heads per kv head
   uint32_t rcp_g;       // div_rcp multipliers of G and NRT
@@ -57,14 +61,14 @@ struct Plan {
 constexpr int kMaxUnits = 1 << 16;
 
 struct AttnArgs {
-  const void* q;        // [B][256][Hq][D]
+  const void* q;        // [B][n_q][Hq][D]
   const void* k_cache;  // [B][cap][Hkv][D]
   const void* v_cache;
-  const void* k_new;    // canvas (step) or block (commit) K/V [B][256][Hkv][D]
+  const void* k_new;    // canvas (step), block (commit) or decode K/V [B][n_q][Hkv][D]
   const void* v_new;
-  void* k_append;       // commit only: cache K/V written at rows L..L+255 (else null)
+  void* k_append;       // commit and decode: cache K/V written at rows L..L+n_q-1 (else null)
   void* v_append;
-  void* out;            // [B][256][Hq][D]
+  void* out;            // [B][n_q][Hq][D]
   void* part_o;         // [n_units][R][D] normalised partial outputs: bf16 for the
                         // bf16 path (the output is rounded to bf16 anyway), fp32 for
                         // the fp32 path
@@ -100,9 +104,15 @@ int launch_attn_fp8(const AttnArgs& a, const Plan& p, bool causal, void* stream)
 int launch_attn_f32(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream);
 int launch_merge(const AttnArgs& a, const Plan& p, int head_dim, bool bf16_out, void* stream);
 int launch_sample(const SampleArgs& s, void* stream);
+int launch_decode(const AttnArgs& a, const Plan& p, int dtype, int head_dim, void* stream);
 
 // Rows per unit of the fp32 kernel and the key granule of every kernel.
 constexpr int kRowsF32 = 64;
 constexpr int kKeyGranule = 32;
+
+// Decode kernel (dg_attn_mfma.hip): 32 packed rows per unit, kDecodeWaves waves that
+// stream their own chunks; one workgroup per CU.
+constexpr int kDecodeRows = 32;
+constexpr int kDecodeWaves = 4;
 
 }  // namespace dg

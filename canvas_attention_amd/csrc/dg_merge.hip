@@ -5,9 +5,9 @@
 // keys is
 //   M = max_s m_s,  w_s = 2^(m_s - M) * l_s,  out = sum_s w_s O_s / sum_s w_s,
 // which is the same softmax as over the concatenated keys: the cache splits and
-// the canvas (or block) tile of one row merge into attention over [cache ;
-// canvas] ("DiffusionGemma Technical Report", paperfeed.app summary, section
-// "The mechanism: an AR model turned inside out").  Splits without keys carry
+// the canvas (or block, or decode) tile of one row merge into attention over
+// [cache ; new rows] ("DiffusionGemma Technical Report", paperfeed.app summary,
+// section "The mechanism: an AR model turned inside out").  Splits without keys carry
 // l_s = 0 and drop out.  Memory-bound: every thread handles one 16-byte chunk
 // of a row (eight bf16 or four fp32 head_dim elements), so partial reads and
 // output writes are contiguous per row.
@@ -35,9 +35,10 @@ __device__ __forceinline__ int div_rcp(int n, uint32_t m) {
 // Partial rows are bf16 for the bf16 path and fp32 for the fp32 path; each thread
 // combines 8 (bf16) or 4 (fp32) adjacent head_dim elements of one row.  Block
 // (x, y) covers rows x*RPB .. of sequence y.  Index math avoids runtime integer
-// division (tens of dependent instructions each, ahead of the first load): G
-// through the plan's reciprocal, the rows per unit (a power of two) by a shift.
-template <int D, bool BF16>
+// division (tens of dependent instructions each, ahead of the first load): G and
+// n_q*G through the plan's reciprocals, the rows per unit (a power of two) by a
+// shift.  DEC: a decode call (n_q rows per head, 1..16) rather than 256.
+template <int D, bool BF16, bool DEC>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
   constexpr int EPT = BF16 ? 8 : 4;  // elements per thread
   constexpr int TPR = D / EPT;       // threads per row
@@ -48,8 +49,10 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
   if (sp.n_splits == 1) return;  // written directly by the attention kernel
   const int rem = xcd_remap(blockIdx.x, gridDim.x) * RPB + threadIdx.x / TPR;  // row of sequence b
   const int dq = threadIdx.x % TPR;
-  if (rem >= Hq * kCanvas) return;
-  const int g = div_rcp(rem / kCanvas, plan.rcp_g), p = rem - g * (kCanvas * G);
+  const int NQ = DEC ? plan.n_q : kCanvas;
+  if (rem >= Hq * NQ) return;
+  const int g = DEC ? div_rcp(rem, plan.rcp_m) : div_rcp(rem / kCanvas, plan.rcp_g);
+  const int p = rem - g * (NQ * G);
   const int rsh = __builtin_ctz((unsigned)plan.rows_per_unit), NRT = plan.n_rowtiles;
   const int rt = p >> rsh, pr = p & (plan.rows_per_unit - 1);
   const int R = plan.rows_per_unit;
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int i = div_rcp(p, plan.rcp_g), hh = p - i * G;
-  const int64_t off = ((int64_t)(b * kCanvas + i) * Hq + g * G + hh) * D + EPT * dq;
+  const int64_t off = ((int64_t)(b * NQ + i) * Hq + g * G + hh) * D + EPT * dq;
   if (BF16) {
     typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
     bf16x8 o;
@@ -116,9 +119,12 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
 template <int D, bool BF16OUT>
 int launch_t(const AttnArgs& a, const Plan& p, hipStream_t st) {
   constexpr int RPB = 256 / (D / (BF16OUT ? 8 : 4));
-  const int rows = a.n_heads_q * kCanvas;  // per sequence
-  hipLaunchKernelGGL((merge_kernel<D, BF16OUT>), dim3((rows + RPB - 1) / RPB, p.batch), dim3(256), 0,
-                     st, a, p);
+  const int rows = a.n_heads_q * p.n_q;  // per sequence
+  const dim3 grid((rows + RPB - 1) / RPB, p.batch);
+  if (p.n_q == kCanvas)
+    hipLaunchKernelGGL((merge_kernel<D, BF16OUT, false>), grid, dim3(256), 0, st, a, p);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, BF16OUT, true>), grid, dim3(256), 0, st, a, p);
   return (int)hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(_HERE, "libdg.so")
 
 DG_BF16, DG_F32, DG_FP8 = 0, 1, 2
 N_CANVAS = 256
+MAX_DECODE = 16
 STATUS = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_DTYPE",
           -4: "DG_ERR_CAPACITY", -5: "DG_ERR_WORKSPACE", -6: "DG_ERR_HIP", -7: "DG_ERR_ALIGN"}
 
@@ -68,6 +69,10 @@ lib.dg_commit_block.restype = _i32
 lib.dg_canvas_step_loop.argtypes = [_P(DgShape), _i32, _vp, _i64, _P(DgKv), _i64, _P(DgKv), _vp,
                                     _vp, _i64, _vp, _sz, _vp]
 lib.dg_canvas_step_loop.restype = _i32
+lib.dg_decode_workspace_bytes.argtypes = [_P(DgShape), _i64]
+lib.dg_decode_workspace_bytes.restype = _sz
+lib.dg_decode_attn.argtypes = [_P(DgShape), _vp, _P(DgKv), _P(DgKv), _vp, _vp, _vp, _sz, _vp]
+lib.dg_decode_attn.restype = _i32
 lib.dg_canvas_sample.argtypes = [_P(DgSampleShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.dg_canvas_sample.restype = _i32
 lib.dg_status_string.argtypes = [_i32]
@@ -84,7 +89,7 @@ lib.dg_kernel_timing_samples.argtypes = [_P(ctypes.c_float), _P(ctypes.c_float),
 lib.dg_kernel_timing_samples.restype = _i32
 
 EXPORTS = ["dg_workspace_bytes", "dg_canvas_attn", "dg_commit_block", "dg_canvas_step_loop",
-           "dg_canvas_sample",
+           "dg_canvas_sample", "dg_decode_workspace_bytes", "dg_decode_attn",
            "dg_status_string", "dg_last_error", "dg_kernel_timing_enable",
            "dg_kernel_timing_read", "dg_kernel_timing_samples"]
 
@@ -212,6 +217,40 @@ def commit_block(q_blk, k_blk, v_blk, k_cache, v_cache, prefix_len, out=None, wo
     _check("dg_commit_block", st)
     return out
 
+
+
+def decode_workspace_bytes(batch, n_new, n_heads_q, n_heads_kv, head_dim, max_prefix_len,
+                           dtype=torch.bfloat16) -> int:
+    """Bytes of workspace any decode call of this shape needs (dg_decode_workspace_bytes)."""
+    shape = DgShape(_dtype_code(dtype), batch, n_new, n_heads_q, n_heads_kv, head_dim, 0.0)
+    return int(lib.dg_decode_workspace_bytes(ctypes.byref(shape), int(max_prefix_len)))
+
+
+def decode_attn(q, k_new, v_new, k_cache, v_cache, prefix_len, out=None, workspace=None,
+                scale=None, stream=None, tensor_scales=None):
+    """dg_decode_attn: k = q.shape[1] new tokens per sequence (1..16) attend causally
+    to the cache and to each other; their K/V are appended to the cache."""
+    dt = q.dtype
+    _need(q, "q", dt, 4)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new),
+                    ("v_new", v_new)):
+        _need(t, name, dt, 4)
+    B, k, Hq, D = q.shape
+    hkv = k_cache.shape[2]
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype(dt), device=q.device)
+    _need(out, "out", out_dtype(dt), 4)
+    if workspace is None:
+        n = decode_workspace_bytes(B, k, Hq, hkv, D, max(int(x) for x in prefix_len), dt)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    shape = _shape(q, hkv, scale, tensor_scales)
+    new = DgKv(k_new.data_ptr(), v_new.data_ptr(), k_new.shape[1])
+    cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])
+    st = lib.dg_decode_attn(ctypes.byref(shape), _ptr(q), ctypes.byref(new), ctypes.byref(cache),
+                            _prefix(prefix_len, B), _ptr(out), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("dg_decode_attn", st)
+    return out
 
 def canvas_step_loop(q_steps, k_steps, v_steps, k_cache, v_cache, prefix_len, out=None,
                      workspace=None, scale=None, stream=None, tensor_scales=None):

@@ -10,6 +10,9 @@
  *   - once a canvas is fully denoised it is frozen, encoded causally and
  *     appended to the cache, so the growing context is never re-encoded
  *     (dg_commit_block).
+ * The same weights also decode causally, token by token, over the same cache
+ * (AR mode, section "The numbers, honestly"; dg_decode_attn, which also takes
+ * several drafted tokens at once for hybrid decoding).
  * The same page (section "The numbers, honestly") and the report's abstract
  * give the block size (256 positions) and the ~12 refinement passes per block
  * that dg_canvas_step_loop is meant for.
@@ -29,7 +32,7 @@
  *
  * Layouts (all row-major, element strides implied by the shape):
  *   queries q, q_blk, out ......... [B][Nc][Hq][D]   (out is bf16 for DG_FP8)
- *   canvas / block K, V ........... [B][Nc][Hkv][D]     (dg_kv.capacity = Nc)
+ *   canvas / block / new K, V ..... [B][Nc][Hkv][D]     (dg_kv.capacity = Nc)
  *   cache K, V .................... [B][capacity][Hkv][D]
  * Query head h reads kv head h / (Hq / Hkv) (grouped-query attention with
  * consecutive query heads sharing a kv head).  prefix_len[b] (host int32
@@ -75,11 +78,13 @@ enum { DG_BF16 = 0, DG_F32 = 1, DG_FP8 = 2 };
 /* Limits checked by every entry point. */
 #define DG_N_CANVAS 256  /* canvas / block length: fixed at 256 positions      */
 #define DG_MAX_BATCH 64  /* sequences per call                                  */
+#define DG_MAX_DECODE 16 /* new tokens per sequence of one dg_decode_attn call  */
 
 typedef struct {
   int32_t dtype;      /* DG_BF16, DG_F32 or DG_FP8                               */
   int32_t batch;      /* B, 1..DG_MAX_BATCH                                      */
-  int32_t n_canvas;   /* Nc, must equal DG_N_CANVAS                              */
+  int32_t n_canvas;   /* Nc, must equal DG_N_CANVAS (dg_decode_attn: the number  */
+                      /* of new tokens k, 1..DG_MAX_DECODE)                      */
   int32_t n_heads_q;  /* Hq >= 1, a multiple of n_heads_kv                       */
   int32_t n_heads_kv; /* Hkv >= 1                                               */
   int32_t head_dim;   /* D: 64 or 128 (DG_FP8: 128)                             */
@@ -163,6 +168,34 @@ dg_status dg_canvas_step_loop(const dg_shape* shape, int32_t n_steps, const void
                               int64_t kv_step_stride, const dg_kv* kv_cache,
                               const int32_t* prefix_len, void* out, int64_t out_step_stride,
                               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Decode attention ("DiffusionGemma Technical Report", paperfeed.app summary,
+ * section "The numbers, honestly": the AR-mode paragraph runs the same weights
+ * causally over the same cache, and the concurrency paragraph serves several
+ * sequences at once).  shape->n_canvas is the number k of new tokens per
+ * sequence, 1..DG_MAX_DECODE: one for plain AR decoding, more for a hybrid
+ * decoder that checks drafted tokens in one pass.  New token i of sequence b
+ * attends to cache rows 0..prefix_len[b]-1 and new rows 0..i (diagonal
+ * included):
+ *   out[b,i,h,:] = softmax_j(scale * <q[b,i,h,:], k_j>) v_j
+ * and the new K/V rows are written, bit for bit, into cache rows
+ * prefix_len[b] .. prefix_len[b]+k-1, as dg_commit_block does for a block.
+ * prefix_len itself is not changed: the caller advances it by the number of
+ * tokens it keeps (rows past the kept ones are overwritten by the next call).
+ * Every element type; head_dim 64 or 128 (DG_FP8: 128).
+ *   q          [B][k][Hq][D] device
+ *   kv_new     device K/V of the new tokens, [B][k][Hkv][D]; capacity must equal k
+ *   kv_cache   device cache; requires prefix_len[b] + k <= capacity
+ *   prefix_len host int32[B]
+ *   out        [B][k][Hq][D] device (bf16 for DG_FP8), written completely
+ *   workspace  device scratch of ws_bytes >= dg_decode_workspace_bytes(shape,
+ *              max_b L_b) (may be NULL when that is 0); contents are overwritten
+ */
+size_t dg_decode_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len);
+dg_status dg_decode_attn(const dg_shape* shape, const void* q, const dg_kv* kv_new,
+                         const dg_kv* kv_cache, const int32_t* prefix_len, void* out,
+                         void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Canvas sampler ("DiffusionGemma Technical Report", paperfeed.app summary,

@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_three_operations():
     names = declared_functions()
-    for n in ("dg_canvas_attn", "dg_commit_block", "dg_canvas_step_loop", "dg_workspace_bytes"):
+    for n in ("dg_canvas_attn", "dg_commit_block", "dg_canvas_step_loop", "dg_workspace_bytes",
+              "dg_decode_attn", "dg_decode_workspace_bytes"):
         assert n in names
 
 
@@ -185,3 +186,50 @@ def test_sample_null_and_alignment(dg):
     assert call_sample(dg, sh, outs=(FAKE, None, FAKE, FAKE, FAKE)) == -1
     assert call_sample(dg, sh, logits=FAKE + 8) == -7
     assert call_sample(dg, sh, prev=FAKE + 2) == -7
+
+
+def call_decode(dg, sh, q=FAKE, new=None, cache=None, prefix=(0,), out=FAKE, ws=FAKE,
+                ws_bytes=1 << 40):
+    new = new or dg.DgKv(FAKE, FAKE, sh.n_canvas)
+    cache = cache or dg.DgKv(FAKE, FAKE, 4096)
+    pl = (ctypes.c_int32 * len(prefix))(*prefix)
+    return dg.lib.dg_decode_attn(ctypes.byref(sh), q, ctypes.byref(new), ctypes.byref(cache), pl,
+                                 out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_canvas=0), -2), (dict(n_canvas=17), -2), (dict(n_canvas=256), -2),
+    (dict(dtype=7, n_canvas=1), -3), (dict(n_canvas=4, head_dim=96), -2),
+    (dict(n_canvas=4, n_heads_q=12), -2), (dict(n_canvas=4, dtype=2, head_dim=64), -2),
+    (dict(n_canvas=2, batch=65), -2),
+])
+def test_decode_shape_errors(dg, kw, code):
+    assert call_decode(dg, shape(dg, **kw)) == code
+
+
+def test_decode_argument_errors(dg):
+    sh = shape(dg, n_canvas=4)
+    assert call_decode(dg, sh, q=None) == -1
+    assert call_decode(dg, sh, new=dg.DgKv(FAKE, None, 4)) == -1
+    assert call_decode(dg, sh, q=FAKE + 4) == -7
+    # the new K/V hold exactly the k new rows
+    assert call_decode(dg, sh, new=dg.DgKv(FAKE, FAKE, 256)) == -2
+    # the cache needs room for the new rows behind the prefix
+    assert call_decode(dg, sh, cache=dg.DgKv(FAKE, FAKE, 100), prefix=(97,)) == -4
+    assert "new tokens" in dg.lib.dg_last_error().decode()
+    assert call_decode(dg, sh, prefix=(-3,)) == -4
+    st = call_decode(dg, sh, prefix=(4000,), ws_bytes=64)
+    assert st == -5 and "workspace" in dg.lib.dg_last_error().decode()
+
+
+def test_decode_workspace_bytes(dg):
+    f = dg.lib.dg_decode_workspace_bytes
+    assert f(ctypes.byref(shape(dg, n_canvas=0)), 100) == 0
+    assert f(ctypes.byref(shape(dg, n_canvas=1)), -1) == 0
+    n1 = f(ctypes.byref(shape(dg, n_canvas=1)), 8192)
+    n16 = f(ctypes.byref(shape(dg, n_canvas=16)), 8192)
+    # 32 packed rows per tile: Hq/Hkv = 2 heads per kv head gives one tile up to 16 tokens
+    assert n1 > 0 and n1 == n16
+    n_g8 = f(ctypes.byref(shape(dg, n_canvas=16, n_heads_q=32, n_heads_kv=4)), 8192)
+    assert n_g8 > n16
+    assert f(ctypes.byref(shape(dg, n_canvas=3, dtype=1, head_dim=64)), 64) > 0
