@@ -12,8 +12,10 @@ and max not counted).  The roofline object is for the dominant kernel (the
 split-key canvas attention kernel), timed with HIP events that the library
 records on its launch stream.  cpu_baseline times the CPU fp64 oracle on a
 bounded sample of the same workload.  The default (bf16) line also carries the
-fp8 canvas step's kernel time and its fraction of the fp8 MFMA peak, and the
-canvas sampler's time per call over one step's logits (--sampler: only that).
+fp8 canvas step's kernel time and its fraction of the fp8 MFMA peak, the
+canvas sampler's time per call over one step's logits (--sampler: only that),
+and decode attention (AR mode, 1 or 16 new tokens over the same cache) on four
+workloads with its own HBM roofline object (--decode [WORKLOAD]: only that).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--dtype fp8]
 """
@@ -40,13 +42,26 @@ ELEM_BYTES = {"bf16": 2, "fp8": 1}
 # the canvas attention kernel of each format, as rocprofv3 names it, and the
 # profile files of its counter summaries
 ATTN_KERNELS = {"bf16": "attn_bf16_kernel<128, false", "fp8": "attn_fp8_kernel<128, false",
-                "sampler": "row_stats_kernel"}
-PROFILE_TAG = {"bf16": "canvas_attn_l8k", "fp8": "canvas_attn_fp8_l8k", "sampler": "canvas_sample_v262k"}
+                "sampler": "row_stats_kernel", "decode": "decode_kernel<dg::(anonymous namespace)::FmtBf16, 128"}
+PROFILE_TAG = {"bf16": "canvas_attn_l8k", "fp8": "canvas_attn_fp8_l8k", "sampler": "canvas_sample_v262k",
+               "decode": "decode_attn_b32_l8k"}
 PROFILE_WHAT = {"bf16": "the canvas attention kernel (bf16; canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)",
                 "fp8": "the canvas attention kernel (fp8; canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)",
-                "sampler": "the sampler's row statistics kernel (B=1, 256 positions, V=262144 bf16 logits)"}
+                "sampler": "the sampler's row statistics kernel (B=1, 256 positions, V=262144 bf16 logits)",
+                "decode": "the decode attention kernel (bf16; 32 sequences at L=8192, one new token each, "
+                          "Hq=16, Hkv=8, D=128)"}
 PROFILE_RUN = {"bf16": "--steps 2 --warmup 1 --profile-steps", "fp8": "--steps 2 --warmup 1 --profile-steps --dtype fp8",
-               "sampler": "--sampler --steps 10"}
+               "sampler": "--sampler --steps 10", "decode": "--decode b32_l8k_k1 --steps 10"}
+
+# Decode attention workloads (AR mode over the same cache; the concurrency
+# crossover of the pages sits near 32 sequences): Hq=16, Hkv=8, D=128, bf16.
+DECODE_WORKLOADS = {
+    "b1_l8k_k1": dict(batch=1, prefix=8192, k=1),
+    "b32_l8k_k1": dict(batch=32, prefix=8192, k=1),
+    "b1_l128k_k1": dict(batch=1, prefix=131072, k=1),
+    "b1_l8k_k16": dict(batch=1, prefix=8192, k=16),
+}
+DECODE_ROOFLINE = "b32_l8k_k1"  # the decode shape whose kernel the roofline object describes
 MOPS_COUNTER = {"bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "fp8": "SQ_INSTS_VALU_MFMA_MOPS_F8"}
 
 
@@ -62,6 +77,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
                   for f in ("dg_attn_mfma.hip", "dg_internal.h")]
 SAMPLER_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
                    for f in ("dg_sample.hip", "dg_internal.h")]
+# the decode kernel shares its source file with the canvas kernels
 
 
 def kernel_source_hash(dtype="bf16"):
@@ -73,8 +89,9 @@ def kernel_source_hash(dtype="bf16"):
 
 
 def measured_traffic(dtype="bf16"):
-    """Bytes per launch of the canvas attention kernel from the counter file, or
-    None when the file is absent or was taken on another version of the kernel."""
+    """Bytes per launch of the kernel behind `dtype` (bf16, fp8, sampler, decode)
+    from its counter file, or None when the file is absent or was taken on
+    another version of the kernel."""
     path = traffic_file(dtype)
     if not os.path.exists(path):
         return None
@@ -85,7 +102,7 @@ def measured_traffic(dtype="bf16"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
     try:
-        if kv["kernel_source_hash"] != kernel_source_hash():
+        if kv["kernel_source_hash"] != kernel_source_hash(dtype):
             return None
         return int(float(kv["traffic_bytes_per_launch"]))
     except (KeyError, ValueError):
@@ -123,7 +140,7 @@ def _counter_per_dispatch(folder, counter, name_part):
 
 def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, dtype="bf16"):
     ATTN_KERNEL = ATTN_KERNELS[dtype]
-    flag = {"bf16": "", "fp8": " --dtype fp8", "sampler": " --sampler"}[dtype]
+    flag = {"bf16": "", "fp8": " --dtype fp8", "sampler": " --sampler", "decode": " --decode"}[dtype]
     copy_bytes = int(copy_mib) * (1 << 20)
     f_kib, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", ATTN_KERNEL)
     w_kib, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", ATTN_KERNEL)
@@ -214,12 +231,15 @@ def summarize_mfma(pass1_dir, pass2_dir, trace_txt, dtype="bf16"):
     print(open(out).read())
 
 
-def summarize_trace(stats_csv, out_txt, dtype="bf16", sampler=False):
+def summarize_trace(stats_csv, out_txt, dtype="bf16", sampler=False, decode=None):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     keep = [r for r in rows if "dg::" in r["Name"] or "copyBuffer" in r["Name"]]
     flag = "" if dtype == "bf16" else f" --dtype {dtype}"
     run = "--sampler --steps 50" if sampler else f"--steps 10 --warmup 2 --no-cpu-baseline{flag}"
+    if decode:
+        run = f"--decode {decode} --steps 20"
+        flag = f" --decode {decode}"
     lines = ["# rocprofv3 --kernel-trace --stats summary (kernels of this library)",
              "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              f"-d <dir> -o run -- python3 <repo>/bench.py {run}",
@@ -298,21 +318,33 @@ class Cycle:
                             out=self.out_steps[s], workspace=self.ws)
 
 
+class Flush:
+    """Evicts L2 and the 256 MB last-level cache by reading a 512 MB buffer (a
+    clean eviction: a write would leave dirty lines whose write-back then runs
+    during the timed kernel and takes about a quarter of its read bandwidth)."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+
+    def __call__(self):
+        self.buf.max()
+
+
 def call_medians(cy, reps, modes=("warm", "cold")):
     """Per-launch kernel durations (the library's events around each launch),
     median over calls of one canvas step (attention + merge): warm (the fixed
     cache stays in the 256 MB last-level cache, as in a block's step loop) and
-    cold (a 512 MB scratch fill before every call, outside the timed kernels)."""
-    import torch
+    cold (a 512 MB read before every call, outside the timed kernels)."""
     dg = cy.dg
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if "cold" in modes else None
+    flush = Flush() if "cold" in modes else None
     medians = {}
     for mode in modes:
         dg.kernel_timing_read()
         dg.kernel_timing_enable(True)
         for i in range(reps):
             if mode == "cold":
-                flush.fill_(i & 255)
+                flush()
             cy.one_step(i)
         a_ms, m_ms = dg.kernel_timing_samples(reps)
         dg.kernel_timing_enable(False)
@@ -450,6 +482,76 @@ def measure_sampler(reps=50, batch=1):
             "kernels": "row_stats_kernel + select_kernel", "timing": f"median of {reps} calls"}
 
 
+
+def decode_bytes(B, L, k, Hq, Hkv, D, esz=2):
+    """Algorithmic bytes of one decode call: the prefix's cache K and V once, the
+    new tokens' Q, K and V, the bf16 output and the appended K/V rows."""
+    return B * (esz * (2 * L * Hkv * D + k * Hq * D + 2 * k * Hkv * D)
+                + 2 * k * Hq * D + esz * 2 * k * Hkv * D)
+
+
+def measure_decode(reps=50, names=None):
+    """Decode attention (dg_decode_attn) per workload: median per call of the decode
+    kernel and of the whole call (kernel + merge) from the library's HIP events,
+    warm (the cache stays in the 256 MB last-level cache between calls) and cold (a
+    512 MB read before every call, outside the timed kernels, as when the model's
+    other layers run between two decode steps).  GB/s and the HBM fraction are the
+    algorithmic bytes over the cold kernel time."""
+    import torch
+    import canvas_attention_amd.dg as dg
+    from canvas_attention_amd import synth
+    Hq, Hkv, D = 16, 8, 128
+    flush = Flush()
+    out = {}
+    for name in names or DECODE_WORKLOADS:
+        w = DECODE_WORKLOADS[name]
+        B, Lv, k = w["batch"], w["prefix"], w["k"]
+        L = np.full(B, Lv, np.int32)
+        kc, vc = synth.cache(1300, L, Lv + k, Hkv, D, "bf16")
+        kc, vc = dev(kc), dev(vc)
+        q, kn, vn = (dev(x) for x in synth.decode(1300, B, k, Hq, Hkv, D, "bf16"))
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(dg.decode_workspace_bytes(B, k, Hq, Hkv, D, Lv), 16), dtype=torch.uint8,
+                         device="cuda")
+
+        def call():
+            dg.decode_attn(q, kn, vn, kc, vc, L, out=o, workspace=ws)
+
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        med = {}
+        for mode in ("warm", "cold"):
+            dg.kernel_timing_read()
+            dg.kernel_timing_enable(True)
+            for i in range(reps):
+                if mode == "cold":
+                    flush()
+                call()
+            a_ms, m_ms = dg.kernel_timing_samples(reps)
+            dg.kernel_timing_enable(False)
+            m_ms = m_ms if len(m_ms) == len(a_ms) else [0.0] * len(a_ms)
+            med[mode] = {"kernel": round(float(np.median(a_ms)) * 1e3, 3),
+                         "call": round(float(np.median(np.add(a_ms, m_ms))) * 1e3, 3)}
+        nbytes = decode_bytes(B, Lv, k, Hq, Hkv, D)
+        gbs = nbytes / (med["cold"]["kernel"] * 1e-6) / 1e9
+        out[name] = {"batch": B, "prefix_len": Lv, "new_tokens": k, "algorithmic_bytes": nbytes,
+                     "kernel_us": {m: med[m]["kernel"] for m in med},
+                     "call_us": {m: med[m]["call"] for m in med},
+                     "cold_kernel_GBps": round(gbs, 1), "cold_kernel_hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        del kc, vc, q, kn, vn, o, ws
+    del flush
+    res = {"workloads": out, "heads": {"n_heads_q": Hq, "n_heads_kv": Hkv, "head_dim": D},
+           "dtype": "bf16", "timing": f"median of {reps} calls per mode"}
+    if DECODE_ROOFLINE in out:
+        r = out[DECODE_ROOFLINE]
+        res["roofline"] = {"bound": "hbm", "achieved": r["cold_kernel_GBps"], "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": r["cold_kernel_hbm_frac"],
+                           "traffic": measured_traffic("decode"),
+                           "kernel": "decode_kernel<FmtBf16,128,4,2> (32 sequences, L=8192, 1 token)",
+                           "algorithmic_bytes_per_launch": r["algorithmic_bytes"]}
+    return res
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,6 +562,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sampler", action="store_true",
                     help="only time the canvas sampler (256 x 262144 bf16 logits per canvas)")
+    ap.add_argument("--decode", nargs="?", const="all", default=None, metavar="WORKLOAD",
+                    help="only time decode attention (all workloads, or the one named: "
+                         + ", ".join(DECODE_WORKLOADS) + ")")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--profile-steps", action="store_true",
@@ -475,10 +580,12 @@ def main():
                     help="write a kernel summary from a rocprofv3 --stats kernel_stats.csv")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, dtype="sampler" if args.sampler else args.dtype)
+        summarize_counters(*args.summarize_counters,
+                           dtype="sampler" if args.sampler else "decode" if args.decode else args.dtype)
         return
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace, dtype=args.dtype, sampler=args.sampler)
+        summarize_trace(*args.summarize_trace, dtype=args.dtype, sampler=args.sampler,
+                        decode=args.decode)
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, dtype=args.dtype)
@@ -497,6 +604,10 @@ def main():
     torch.cuda.set_device(0)
     if args.sampler:
         print(json.dumps({"sampler": measure_sampler(max(args.steps, 10))}), flush=True)
+        return
+    if args.decode:
+        names = None if args.decode == "all" else [args.decode]
+        print(json.dumps({"decode": measure_decode(max(args.steps, 10), names)}), flush=True)
         return
     m = measure(args.dtype, args.steps, args.warmup, args.profile_steps)
     if args.profile_steps:
@@ -522,6 +633,7 @@ def main():
     if args.dtype == "bf16":
         result["fp8"] = fp8_summary()
         result["sampler"] = measure_sampler()
+        result["decode"] = measure_decode()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline("cycle_l8k", args.cpu_seconds, args.dtype)
     print(json.dumps(result), flush=True)

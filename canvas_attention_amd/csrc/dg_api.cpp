@@ -218,7 +218,7 @@ void make_decode_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
   p->batch = s->batch;
   p->n_q = nq;
   p->rcp_m = dg::rcp_u32((uint32_t)(nq * G));
-  p->variant = dg::kDefaultVariant;
+  p->variant = dg::kDefaultVariant;  // unused by the decode kernel
   p->n_rowtiles = NRT;
   p->rows_per_unit = R;
   p->g = G;

@@ -1434,6 +1434,8 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(AttnArgs a, Plan plan) 
   static_assert(IPT % 4 == 0, "tiles of whole 4 KB load groups");
   constexpr int NG = IPT / 4;
   constexpr int PERCH = 2 * IPT;    // loads per chunk (K and V)
+  // outstanding loads issued after the loads of the chunk being waited for
+  constexpr int AFTER = (NST - 1) * PERCH;
   static_assert(NST >= 2 && NST * PERCH <= 63, "outstanding loads within the vmcnt range");
   constexpr int SLOTB = 2 * TILEB;  // one stage: K tile, then V tile
   constexpr int WAVEB = NST * SLOTB;
@@ -1469,17 +1471,31 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(AttnArgs a, Plan plan) 
   const char* vn = (const char*)a.v_new + ((int64_t)u.b * NQ * Hkv + u.g) * ROWB;
 
   // ---- the cache append, first half: load the new rows of head g
+  // (one named register per chunk: an array here is placed in LDS or scratch)
   const bool appender = a.k_append != nullptr && u.s == 0 && u.rt == 0;
   const int napp = appender ? 2 * NQ * CH : 0;  // 16-byte chunks of K and V
-  uint4 app[APT];
-#pragma unroll
-  for (int r = 0; r < APT; r++) {
+  static_assert(APT <= 4, "at most four appended chunks per thread");
+  auto app_load = [&](int r) {
+    const int idx = tid + NT * r;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (idx < napp) {
+      const int which = idx >= NQ * CH, rem = idx - which * NQ * CH;
+      v = *(const uint4*)((which ? vn : kn) + (int64_t)(rem / CH) * rsb + 16 * (rem % CH));
+    }
+    return v;
+  };
+  auto app_store = [&](int r, uint4 v) {
     const int idx = tid + NT * r;
     if (idx < napp) {
       const int which = idx >= NQ * CH, rem = idx - which * NQ * CH;
-      app[r] = *(const uint4*)((which ? vn : kn) + (int64_t)(rem / CH) * rsb + 16 * (rem % CH));
+      const int64_t dst = ((int64_t)u.b * a.cap * Hkv + u.g) * ROWB + (int64_t)(L + rem / CH) * rsb + 16 * (rem % CH);
+      *(uint4*)((char*)(which ? a.v_append : a.k_append) + dst) = v;
     }
-  }
+  };
+  const uint4 app0 = app_load(0);
+  const uint4 app1 = APT > 1 ? app_load(1) : app0;
+  const uint4 app2 = APT > 2 ? app_load(2) : app0;
+  const uint4 app3 = APT > 3 ? app_load(3) : app0;
 
   const uint32_t lbase = lds_addr(lds);
   const uint32_t qarea = lbase + NW * WAVEB;
@@ -1563,12 +1579,13 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(AttnArgs a, Plan plan) 
 #pragma unroll
   for (int mb = 0; mb < MB; mb++) vaddr[mb] = wring + TILEB + lo.v[mb];
 
-  // ---- prologue: the first NST chunks of this wave, then the query tile
+  // ---- prologue: the first NST chunks of this wave, then the query tile together
+  //      with chunk 0
 #pragma unroll
   for (int c = 0; c < NST; c++)
     if (c < nmine) issue_chunk(c, wring + c * SLOTB);
   if (nmine >= NST)
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NST * PERCH) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(AFTER) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   if constexpr (F8) {
@@ -1598,7 +1615,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(AttnArgs a, Plan plan) 
       const int c = c0 + j;
       if (c >= nmine) break;
       if (c + NST <= nmine)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 1) * PERCH) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(AFTER) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       const uint32_t off = (uint32_t)j * SLOTB;
@@ -1618,15 +1635,10 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(AttnArgs a, Plan plan) 
   if constexpr (F8) acc.lsum = h == 0 ? op.rs[0] : 0.f;
 
   // ---- the cache append, second half
-#pragma unroll
-  for (int r = 0; r < APT; r++) {
-    const int idx = tid + NT * r;
-    if (idx < napp) {
-      const int which = idx >= NQ * CH, rem = idx - which * NQ * CH;
-      const int64_t dst = ((int64_t)u.b * a.cap * Hkv + u.g) * ROWB + (int64_t)(L + rem / CH) * rsb + 16 * (rem % CH);
-      *(uint4*)((char*)(which ? a.v_append : a.k_append) + dst) = app[r];
-    }
-  }
+  app_store(0, app0);
+  if (APT > 1) app_store(1, app1);
+  if (APT > 2) app_store(2, app2);
+  if (APT > 3) app_store(3, app3);
 
   // ---- merge the waves: waves 1.. leave their state in their own ring (all of
   //      their loads and reads are complete), wave 0 folds it in
@@ -1731,6 +1743,7 @@ int launch_attn_fp8(const AttnArgs& a, const Plan& p, bool causal, void* stream)
 int launch_decode(const AttnArgs& a, const Plan& p, int dtype, int head_dim, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (p.n_units == 0) return 0;
+  // two stages of 16 KB (K and V chunk) per wave at head_dim 128, four of 8 KB at 64
   if (dtype == DG_FP8) return launch_decode_t<FmtFp8, 128, 2>(a, p, st);
   if (head_dim == 128) return launch_decode_t<FmtBf16, 128, 2>(a, p, st);
   return launch_decode_t<FmtBf16, 64, 4>(a, p, st);
