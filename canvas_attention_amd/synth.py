@@ -7,7 +7,8 @@ and the CPU oracle consume exactly the arrays produced here.
 Recipe (the same for every workload):
   * generator: ``numpy.random.default_rng([seed, tensor_id, seq, block, step])``
     with one seed per workload and tensor ids 0/1 cache K/V, 2/3/4 canvas Q/K/V,
-    5/6/7 commit (block) Q/K/V, 11/12/13 decode Q/K/V;
+    5/6/7 commit (block) Q/K/V, 11/12/13 decode Q/K/V, 14/15/16 the
+    self-conditioning embedding table and MLP weights;
   * values: ``standard_normal`` drawn in float32, stored as bf16 by rounding to
     nearest-even (fp32 workloads keep the float32 values; fp8 workloads store
     OCP e4m3 bytes, rounded to nearest-even, with tensor scales of 1);
@@ -29,6 +30,7 @@ N_CANVAS = 256
 T_CACHE_K, T_CACHE_V, T_Q, T_K, T_V, T_QB, T_KB, T_VB = range(8)
 T_LOGITS, T_NOISE, T_PEAK = 8, 9, 10   # canvas sampler inputs
 T_QD, T_KD, T_VD = 11, 12, 13          # decode Q/K/V of the new tokens
+T_EMB, T_W1, T_W2 = 14, 15, 16          # self-conditioning weights (embedding table, MLP)
 
 VOCAB = 262144  # vocabulary of the sampled model family ("262k vocabulary")
 
@@ -165,6 +167,23 @@ def decode(seed: int, batch: int, n_new: int, hq: int, hkv: int, d: int, dtype: 
     k = batched(seed, T_KD, batch, n_new, hkv, d, dtype, 0, step)
     v = batched(seed, T_VD, batch, n_new, hkv, d, dtype, 0, step)
     return q, k, v
+
+
+def selfcond_weights(seed: int, vocab: int, d: int, h: int):
+    """Synthetic self-conditioning weights as bf16 bits: the embedding table E
+    [V, d] ~ N(0, 1), and the MLP's W1 [d, h] ~ N(0, 1/d) and W2 [h, d] ~ N(0, 1/h)
+    (unit-variance activations through both layers).  E is drawn in slabs of 8192
+    rows so that memory stays bounded at large vocabularies."""
+    E = np.empty((vocab, d), np.uint16)
+    for v0 in range(0, vocab, 8192):
+        rng = np.random.default_rng([seed, T_EMB, v0 // 8192])
+        n = min(8192, vocab - v0)
+        E[v0:v0 + n] = bf16_round(rng.standard_normal((n, d), dtype=np.float32))
+    w1 = bf16_round(np.random.default_rng([seed, T_W1]).standard_normal((d, h), dtype=np.float32)
+                    / np.float32(np.sqrt(d)))
+    w2 = bf16_round(np.random.default_rng([seed, T_W2]).standard_normal((h, d), dtype=np.float32)
+                    / np.float32(np.sqrt(h)))
+    return E, w1, w2
 
 
 def sampler_logits(seed: int, batch: int, vocab: int = VOCAB, step: int = 0) -> np.ndarray:
