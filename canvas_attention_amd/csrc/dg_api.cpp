@@ -538,6 +538,93 @@ dg_status dg_canvas_sample(const dg_sample_shape* shape, const void* logits,
   return DG_OK;
 }
 
+// Workspace layout of dg_self_condition: every part 256-byte aligned.
+struct SelfcondLayout {
+  size_t pblk, stats, part, yblk, hblk, total;
+  int vocab_splits, split_w1, split_w2;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static dg_status selfcond_layout(const dg_selfcond_shape* s, SelfcondLayout* l) {
+  if (!s) return fail(DG_ERR_NULL, "shape is NULL");
+  if (s->batch < 1 || s->batch > DG_MAX_BATCH)
+    return fail(DG_ERR_SHAPE, "batch %d outside 1..%d", s->batch, DG_MAX_BATCH);
+  if (s->n_canvas != DG_N_CANVAS)
+    return fail(DG_ERR_SHAPE, "n_canvas %d, must be %d", s->n_canvas, DG_N_CANVAS);
+  if (s->vocab < dg::kSelfcondBlock || s->vocab % dg::kSelfcondBlock != 0 ||
+      s->vocab > DG_SELFCOND_MAX_VOCAB)
+    return fail(DG_ERR_SHAPE, "vocab %d: a multiple of 32 in 32..%d", s->vocab, DG_SELFCOND_MAX_VOCAB);
+  if (s->d_model < 128 || s->d_model % 128 != 0 || s->d_model > 16384)
+    return fail(DG_ERR_SHAPE, "d_model %d: a multiple of 128 in 128..16384", s->d_model);
+  if (s->d_hidden < 128 || s->d_hidden % 128 != 0 || s->d_hidden > 16384)
+    return fail(DG_ERR_SHAPE, "d_hidden %d: a multiple of 128 in 128..16384", s->d_hidden);
+  const size_t M = (size_t)s->batch * DG_N_CANVAS;
+  const int cus = device_cu_count();
+  l->vocab_splits = (s->vocab + dg::kSelfcondSplit - 1) / dg::kSelfcondSplit;
+  l->split_w1 = dg::selfcond_splits(s->d_model, s->d_hidden, (int)M, cus);
+  l->split_w2 = dg::selfcond_splits(s->d_hidden, s->d_model, (int)M, cus);
+  const size_t s1 = (size_t)l->vocab_splits;
+  const size_t s2 = (size_t)((s->d_model + l->split_w1 - 1) / l->split_w1);
+  const size_t s3 = (size_t)((s->d_hidden + l->split_w2 - 1) / l->split_w2);
+  const size_t part = std::max({s1 * M * s->d_model, s2 * M * s->d_hidden, s3 * M * s->d_model}) * 4;
+  l->pblk = 0;
+  l->stats = align256(l->pblk + M * s->vocab * 2);
+  l->part = align256(l->stats + s1 * M * 8);
+  l->yblk = align256(l->part + part);
+  l->hblk = align256(l->yblk + M * s->d_model * 2);
+  l->total = align256(l->hblk + M * s->d_hidden * 2);
+  return DG_OK;
+}
+
+static void hook_begin(int kind, hipStream_t st) { time_begin(kind, st); }
+static void hook_end(int kind, hipStream_t st) { time_end(kind, st); }
+
+size_t dg_selfcond_workspace_bytes(const dg_selfcond_shape* shape) {
+  SelfcondLayout l;
+  return selfcond_layout(shape, &l) == DG_OK ? l.total : 0;
+}
+
+dg_status dg_self_condition(const dg_selfcond_shape* shape, const void* logits, const void* embed,
+                            const void* w1, const void* w2, void* z, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  SelfcondLayout l;
+  dg_status st = selfcond_layout(shape, &l);
+  if (st) return st;
+  if (!logits || !embed || !w1 || !w2 || !z || !workspace)
+    return fail(DG_ERR_NULL, "a required argument is NULL (logits, embed, w1, w2, z, workspace)");
+  const void* ptrs[] = {logits, embed, w1, w2, z, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(DG_ERR_ALIGN, "device pointer %p is not 16-byte aligned", p);
+  if (ws_bytes < l.total)
+    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes, this call needs %zu", ws_bytes, l.total);
+  dg::SelfcondArgs a;
+  char* ws = (char*)workspace;
+  a.logits = logits;
+  a.embed = embed;
+  a.w1 = w1;
+  a.w2 = w2;
+  a.z = z;
+  a.pblk = ws + l.pblk;
+  a.stats = (float2*)(ws + l.stats);
+  a.part = (float*)(ws + l.part);
+  a.yblk = ws + l.yblk;
+  a.hblk = ws + l.hblk;
+  a.rows = shape->batch * DG_N_CANVAS;
+  a.vocab = shape->vocab;
+  a.vocab_splits = l.vocab_splits;
+  a.d_model = shape->d_model;
+  a.d_hidden = shape->d_hidden;
+  a.split_w1 = l.split_w1;
+  a.split_w2 = l.split_w2;
+  a.time_begin = hook_begin;
+  a.time_end = hook_end;
+  const int err = dg::launch_selfcond(a, stream);
+  if (err != 0)
+    return fail(DG_ERR_HIP, "self-conditioning launch failed: %s", hipGetErrorString((hipError_t)err));
+  return DG_OK;
+}
+
 const char* dg_status_string(dg_status status) {
   switch (status) {
     case DG_OK: return "DG_OK";

@@ -11,6 +11,7 @@
 // result (normalised output rows plus log2-domain max and sum) that a merge
 // kernel combines; a sequence with a single split writes its output directly.
 #pragma once
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "dg.h"
@@ -97,6 +98,28 @@ struct SampleArgs {
   int32_t batch;
 };
 
+// Self-conditioning input (dg_selfcond.hip).  The softmax pass works on vocabulary
+// splits of kSelfcondSplit entries and writes blocks of kSelfcondBlock entries.
+constexpr int kSelfcondSplit = 8192;
+constexpr int kSelfcondBlock = 32;
+
+struct SelfcondArgs {
+  const void* logits;  // [M][V] bf16, M = B*256 rows
+  const void* embed;   // [V][d] bf16
+  const void* w1;      // [d][h] bf16
+  const void* w2;      // [h][d] bf16
+  void* z;             // [M][d] bf16 out
+  void* pblk;          // workspace: exp(x - split max) as bf16, blocked [V/32][M][32]
+  float2* stats;       // workspace: [V/8192][M] (log2-domain split max, sum of the weights)
+  float* part;         // workspace: fp32 split partials of the products
+  void* yblk;          // workspace: softmax(x) E as bf16, blocked [d/32][M][32]
+  void* hblk;          // workspace: gelu(y W1) as bf16, blocked [h/32][M][32]
+  int32_t rows, vocab, vocab_splits, d_model, d_hidden, split_w1, split_w2;
+  // kernel timing hooks of the library (kind 0: the embedding product, 1: the softmax pass)
+  void (*time_begin)(int kind, hipStream_t st);
+  void (*time_end)(int kind, hipStream_t st);
+};
+
 // Host-side launchers (defined next to their kernels).  Each returns the HIP
 // error of the launch.
 int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream);
@@ -105,6 +128,9 @@ int launch_attn_f32(const AttnArgs& a, const Plan& p, int head_dim, bool causal,
 int launch_merge(const AttnArgs& a, const Plan& p, int head_dim, bool bf16_out, void* stream);
 int launch_sample(const SampleArgs& s, void* stream);
 int launch_decode(const AttnArgs& a, const Plan& p, int dtype, int head_dim, void* stream);
+int launch_selfcond(const SelfcondArgs& a, void* stream);
+// contraction rows per split of a self-conditioning product (a multiple of 32)
+int selfcond_splits(int K, int N, int M, int cus);
 
 // Rows per unit of the fp32 kernel and the key granule of every kernel.
 constexpr int kRowsF32 = 64;

@@ -43,6 +43,11 @@ class DgSampleShape(ctypes.Structure):
                 ("stop_entropy", ctypes.c_float)]
 
 
+class DgSelfcondShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_canvas", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("d_model", ctypes.c_int32), ("d_hidden", ctypes.c_int32)]
+
+
 class DgKv(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
 
@@ -73,6 +78,10 @@ lib.dg_decode_workspace_bytes.argtypes = [_P(DgShape), _i64]
 lib.dg_decode_workspace_bytes.restype = _sz
 lib.dg_decode_attn.argtypes = [_P(DgShape), _vp, _P(DgKv), _P(DgKv), _vp, _vp, _vp, _sz, _vp]
 lib.dg_decode_attn.restype = _i32
+lib.dg_selfcond_workspace_bytes.argtypes = [_P(DgSelfcondShape)]
+lib.dg_selfcond_workspace_bytes.restype = _sz
+lib.dg_self_condition.argtypes = [_P(DgSelfcondShape), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+lib.dg_self_condition.restype = _i32
 lib.dg_canvas_sample.argtypes = [_P(DgSampleShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.dg_canvas_sample.restype = _i32
 lib.dg_status_string.argtypes = [_i32]
@@ -90,6 +99,7 @@ lib.dg_kernel_timing_samples.restype = _i32
 
 EXPORTS = ["dg_workspace_bytes", "dg_canvas_attn", "dg_commit_block", "dg_canvas_step_loop",
            "dg_canvas_sample", "dg_decode_workspace_bytes", "dg_decode_attn",
+           "dg_selfcond_workspace_bytes", "dg_self_condition",
            "dg_status_string", "dg_last_error", "dg_kernel_timing_enable",
            "dg_kernel_timing_read", "dg_kernel_timing_samples"]
 
@@ -311,6 +321,38 @@ def canvas_sample(logits, noise_tokens, prev_argmax=None, tau=0.8, budget=0.1,
     _check("dg_canvas_sample", st)
     return entropy, argmax, tokens, accepted, stop
 
+
+
+def selfcond_workspace_bytes(batch, vocab, d_model, d_hidden) -> int:
+    """Bytes of workspace a self-conditioning call of this shape needs."""
+    shape = DgSelfcondShape(batch, N_CANVAS, vocab, d_model, d_hidden)
+    return int(lib.dg_selfcond_workspace_bytes(ctypes.byref(shape)))
+
+
+def self_condition(logits, embed, w1, w2, out=None, workspace=None, stream=None):
+    """dg_self_condition: z = gelu(softmax(logits) E W1) W2 for bf16 logits
+    [B, 256, V], E [V, d], W1 [d, h], W2 [h, d]; returns z [B, 256, d] bf16."""
+    _need(logits, "logits", torch.bfloat16, 3)
+    _need(embed, "embed", torch.bfloat16, 2)
+    _need(w1, "w1", torch.bfloat16, 2)
+    _need(w2, "w2", torch.bfloat16, 2)
+    B, nc, V = logits.shape
+    d, h = w1.shape
+    if embed.shape != (V, d) or w2.shape != (h, d):
+        raise ValueError(f"shapes: logits {tuple(logits.shape)}, embed {tuple(embed.shape)}, "
+                         f"w1 {tuple(w1.shape)}, w2 {tuple(w2.shape)}")
+    if out is None:
+        out = torch.empty((B, nc, d), dtype=torch.bfloat16, device=logits.device)
+    _need(out, "out", torch.bfloat16, 3)
+    shape = DgSelfcondShape(B, nc, V, d, h)
+    if workspace is None:
+        n = int(lib.dg_selfcond_workspace_bytes(ctypes.byref(shape)))
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=logits.device)
+    st = lib.dg_self_condition(ctypes.byref(shape), _ptr(logits), _ptr(embed), _ptr(w1), _ptr(w2),
+                               _ptr(out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("dg_self_condition", st)
+    return out
 
 def kernel_timing_enable(on: bool = True):
     _check("dg_kernel_timing_enable", lib.dg_kernel_timing_enable(1 if on else 0))

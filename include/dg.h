@@ -12,7 +12,10 @@
  *     (dg_commit_block).
  * The same weights also decode causally, token by token, over the same cache
  * (AR mode, section "The numbers, honestly"; dg_decode_attn, which also takes
- * several drafted tokens at once for hybrid decoding).
+ * several drafted tokens at once for hybrid decoding).  After each step the
+ * sampler (dg_canvas_sample) accepts or re-noises positions, and the predicted
+ * distribution feeds the next step through the self-conditioning input
+ * (dg_self_condition).
  * The same page (section "The numbers, honestly") and the report's abstract
  * give the block size (256 positions) and the ~12 refinement passes per block
  * that dg_canvas_step_loop is meant for.
@@ -235,6 +238,45 @@ dg_status dg_canvas_sample(const dg_sample_shape* shape, const void* logits,
                            const int32_t* noise_tokens, const int32_t* prev_argmax,
                            float* entropy, int32_t* argmax, int32_t* tokens,
                            int32_t* accepted, int32_t* stop, void* stream);
+
+/*
+ * Self-conditioning input ("DiffusionGemma Technical Report", paperfeed.app
+ * summary, section "The mechanism: an AR model turned inside out",
+ * self-conditioning paragraph): next to the noisy canvas the decoder receives
+ * z = FFW(p0 E), the previous step's predicted token distribution p0 pushed
+ * through the embedding matrix E and a small MLP.  Readings of what the page
+ * leaves open: p0 = softmax(logits) at temperature 1 (the annealed temperature
+ * belongs to the sampler); FFW(y) = gelu(y W1) W2 with no biases and GELU in its
+ * tanh form.  For every sequence b and canvas position i:
+ *   y[b,i,:] = sum_v softmax(logits[b,i,:])_v E[v,:]
+ *   z[b,i,:] = gelu(y[b,i,:] W1) W2
+ * Precision: p0, y and gelu(y W1) are rounded to bf16 before the product that
+ * consumes them; products accumulate in fp32; z is bf16.
+ *   logits     [B][Nc][V] bf16 device; finite or -inf (a row needs one finite value)
+ *   embed      E [V][d] bf16 device
+ *   w1         [d][h] bf16 device;  w2 [h][d] bf16 device
+ *   z          [B][Nc][d] bf16 device (out)
+ *   workspace  device scratch of ws_bytes >= dg_selfcond_workspace_bytes(shape)
+ *              (the blocked softmax weights, split partials, y and the hidden
+ *              activations); contents are overwritten
+ * All pointers 16-byte aligned.  Seven kernel launches on `stream`.  With
+ * dg_kernel_timing_enable, the embedding product is recorded in the attention
+ * slot and the softmax pass in the merge slot.
+ */
+#define DG_SELFCOND_MAX_VOCAB 524288
+
+typedef struct {
+  int32_t batch;     /* B, 1..DG_MAX_BATCH                                        */
+  int32_t n_canvas;  /* Nc, must equal DG_N_CANVAS                                */
+  int32_t vocab;     /* V, a multiple of 32, 32..DG_SELFCOND_MAX_VOCAB            */
+  int32_t d_model;   /* d, a multiple of 128, 128..16384                          */
+  int32_t d_hidden;  /* h, the MLP's hidden width, a multiple of 128, 128..16384  */
+} dg_selfcond_shape;
+
+size_t dg_selfcond_workspace_bytes(const dg_selfcond_shape* shape);
+dg_status dg_self_condition(const dg_selfcond_shape* shape, const void* logits, const void* embed,
+                            const void* w1, const void* w2, void* z, void* workspace,
+                            size_t ws_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* dg_status_string(dg_status status);

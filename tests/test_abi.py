@@ -233,3 +233,31 @@ def test_decode_workspace_bytes(dg):
     n_g8 = f(ctypes.byref(shape(dg, n_canvas=16, n_heads_q=32, n_heads_kv=4)), 8192)
     assert n_g8 > n16
     assert f(ctypes.byref(shape(dg, n_canvas=3, dtype=1, head_dim=64)), 64) > 0
+
+
+def sc_shape(dg, **kw):
+    d = dict(batch=1, n_canvas=256, vocab=262144, d_model=2048, d_hidden=1920)
+    d.update(kw)
+    return dg.DgSelfcondShape(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), -2), (dict(n_canvas=255), -2), (dict(vocab=100), -2), (dict(vocab=16), -2),
+    (dict(vocab=524288 + 32), -2), (dict(d_model=200), -2), (dict(d_hidden=0), -2),
+])
+def test_selfcond_shape_errors(dg, kw, code):
+    sh = sc_shape(dg, **kw)
+    assert dg.lib.dg_selfcond_workspace_bytes(ctypes.byref(sh)) == 0
+    st = dg.lib.dg_self_condition(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == code
+
+
+def test_selfcond_argument_errors(dg):
+    sh = sc_shape(dg)
+    n = dg.lib.dg_selfcond_workspace_bytes(ctypes.byref(sh))
+    # the blocked softmax weights alone are 256 x 262144 bf16
+    assert n >= 256 * 262144 * 2
+    f = dg.lib.dg_self_condition
+    assert f(ctypes.byref(sh), None, FAKE, FAKE, FAKE, FAKE, FAKE, n, None) == -1
+    assert f(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, n, None) == -7
+    assert f(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n - 1, None) == -5
