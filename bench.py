@@ -14,8 +14,10 @@ records on its launch stream.  cpu_baseline times the CPU fp64 oracle on a
 bounded sample of the same workload.  The default (bf16) line also carries the
 fp8 canvas step's kernel time and its fraction of the fp8 MFMA peak, the
 canvas sampler's time per call over one step's logits (--sampler: only that),
-and decode attention (AR mode, 1 or 16 new tokens over the same cache) on four
-workloads with its own HBM roofline object (--decode [WORKLOAD]: only that).
+decode attention (AR mode, 1 or 16 new tokens over the same cache) on four
+workloads with its own HBM roofline object (--decode [WORKLOAD]: only that), and
+the self-conditioning input z = FFW(softmax(logits) E) of one canvas with the
+roofline of its embedding product (--selfcond: only that).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--dtype fp8]
 """
@@ -42,16 +44,20 @@ ELEM_BYTES = {"bf16": 2, "fp8": 1}
 # the canvas attention kernel of each format, as rocprofv3 names it, and the
 # profile files of its counter summaries
 ATTN_KERNELS = {"bf16": "attn_bf16_kernel<128, false", "fp8": "attn_fp8_kernel<128, false",
-                "sampler": "row_stats_kernel", "decode": "decode_kernel<dg::(anonymous namespace)::FmtBf16, 128"}
+                "sampler": "row_stats_kernel", "decode": "decode_kernel<dg::(anonymous namespace)::FmtBf16, 128",
+                "selfcond": "gemm_kernel<256>"}
 PROFILE_TAG = {"bf16": "canvas_attn_l8k", "fp8": "canvas_attn_fp8_l8k", "sampler": "canvas_sample_v262k",
-               "decode": "decode_attn_b32_l8k"}
+               "decode": "decode_attn_b32_l8k", "selfcond": "selfcond_v262k_d2048"}
 PROFILE_WHAT = {"bf16": "the canvas attention kernel (bf16; canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)",
                 "fp8": "the canvas attention kernel (fp8; canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)",
                 "sampler": "the sampler's row statistics kernel (B=1, 256 positions, V=262144 bf16 logits)",
                 "decode": "the decode attention kernel (bf16; 32 sequences at L=8192, one new token each, "
-                          "Hq=16, Hkv=8, D=128)"}
+                          "Hq=16, Hkv=8, D=128)",
+                "selfcond": "the self-conditioning embedding product (256 x 262144 softmax weights times "
+                            "E [262144 x 2048], bf16)"}
 PROFILE_RUN = {"bf16": "--steps 2 --warmup 1 --profile-steps", "fp8": "--steps 2 --warmup 1 --profile-steps --dtype fp8",
-               "sampler": "--sampler --steps 10", "decode": "--decode b32_l8k_k1 --steps 10"}
+               "sampler": "--sampler --steps 10", "decode": "--decode b32_l8k_k1 --steps 10",
+               "selfcond": "--selfcond --steps 10"}
 
 # Decode attention workloads (AR mode over the same cache; the concurrency
 # crossover of the pages sits near 32 sequences): Hq=16, Hkv=8, D=128, bf16.
@@ -77,12 +83,15 @@ KERNEL_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
                   for f in ("dg_attn_mfma.hip", "dg_internal.h")]
 SAMPLER_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
                    for f in ("dg_sample.hip", "dg_internal.h")]
+SELFCOND_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
+                    for f in ("dg_selfcond.hip", "dg_internal.h")]
 # the decode kernel shares its source file with the canvas kernels
 
 
 def kernel_source_hash(dtype="bf16"):
     h = hashlib.sha256()
-    for f in SAMPLER_SOURCES if dtype == "sampler" else KERNEL_SOURCES:
+    srcs = {"sampler": SAMPLER_SOURCES, "selfcond": SELFCOND_SOURCES}.get(dtype, KERNEL_SOURCES)
+    for f in srcs:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -140,7 +149,8 @@ def _counter_per_dispatch(folder, counter, name_part):
 
 def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, dtype="bf16"):
     ATTN_KERNEL = ATTN_KERNELS[dtype]
-    flag = {"bf16": "", "fp8": " --dtype fp8", "sampler": " --sampler", "decode": " --decode"}[dtype]
+    flag = {"bf16": "", "fp8": " --dtype fp8", "sampler": " --sampler", "decode": " --decode",
+            "selfcond": " --selfcond"}[dtype]
     copy_bytes = int(copy_mib) * (1 << 20)
     f_kib, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", ATTN_KERNEL)
     w_kib, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", ATTN_KERNEL)
@@ -231,7 +241,7 @@ def summarize_mfma(pass1_dir, pass2_dir, trace_txt, dtype="bf16"):
     print(open(out).read())
 
 
-def summarize_trace(stats_csv, out_txt, dtype="bf16", sampler=False, decode=None):
+def summarize_trace(stats_csv, out_txt, dtype="bf16", sampler=False, decode=None, selfcond=False):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     keep = [r for r in rows if "dg::" in r["Name"] or "copyBuffer" in r["Name"]]
@@ -240,6 +250,9 @@ def summarize_trace(stats_csv, out_txt, dtype="bf16", sampler=False, decode=None
     if decode:
         run = f"--decode {decode} --steps 20"
         flag = f" --decode {decode}"
+    if selfcond:
+        run = "--selfcond --steps 20"
+        flag = " --selfcond"
     lines = ["# rocprofv3 --kernel-trace --stats summary (kernels of this library)",
              "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              f"-d <dir> -o run -- python3 <repo>/bench.py {run}",
@@ -552,6 +565,68 @@ def measure_decode(reps=50, names=None):
                            "algorithmic_bytes_per_launch": r["algorithmic_bytes"]}
     return res
 
+
+SELFCOND_SHAPE = dict(batch=1, vocab=262144, d_model=2048, d_hidden=1920)
+
+
+def measure_selfcond(reps=20):
+    """The self-conditioning input (dg_self_condition) for one canvas: 256 positions,
+    the 262144-token vocabulary, d=2048, MLP hidden width 1920 (7.86M parameters).
+    Median per call (torch events on the launch stream) and per kernel (the
+    library's events: the embedding product and the softmax pass).  The embedding
+    product's algorithmic bytes are E and the softmax weights (bf16) once; its
+    algorithmic FLOP 2*256*V*d."""
+    import torch
+    import canvas_attention_amd.dg as dg
+    from canvas_attention_amd import synth
+    sh = SELFCOND_SHAPE
+    B, V, d, h = sh["batch"], sh["vocab"], sh["d_model"], sh["d_hidden"]
+    lg = dev(synth.sampler_logits(1006, B, vocab=V))
+    E, w1, w2 = (dev(x) for x in synth.selfcond_weights(1400, V, d, h))
+    z = torch.empty((B, 256, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(dg.selfcond_workspace_bytes(B, V, d, h), dtype=torch.uint8, device="cuda")
+
+    def call():
+        dg.self_condition(lg, E, w1, w2, out=z, workspace=ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    dg.kernel_timing_read()
+    dg.kernel_timing_enable(True)
+    for _ in range(reps):
+        call()
+    gemm_ms, soft_ms = dg.kernel_timing_samples(reps)
+    dg.kernel_timing_enable(False)
+    call_us = float(np.median(ts)) * 1e3
+    gemm_us = float(np.median(gemm_ms)) * 1e3
+    soft_us = float(np.median(soft_ms)) * 1e3
+    M = B * 256
+    nbytes = V * d * 2 + M * V * 2
+    flop = 2.0 * M * V * d
+    gbs = nbytes / (gemm_us * 1e-6) / 1e9
+    tfl = flop / (gemm_us * 1e-6) / 1e12
+    return {"batch": B, "vocab": V, "d_model": d, "d_hidden": h, "call_us_median": round(call_us, 2),
+            "positions_per_s": round(M / (call_us * 1e-6), 1),
+            "kernels_us": {"embedding_product": round(gemm_us, 2), "softmax": round(soft_us, 2)},
+            "softmax_GBps": round(2 * M * V * 2 / (soft_us * 1e-6) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("selfcond"),
+                         "kernel": "gemm_kernel<256> (embedding product, 256 x 262144 x 2048)",
+                         "algorithmic_bytes_per_launch": nbytes,
+                         "mfma_tflops": round(tfl, 1), "mfma_frac": round(tfl / PEAK_TFLOPS["bf16"], 4)},
+            "timing": f"median of {reps} calls"}
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -562,6 +637,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sampler", action="store_true",
                     help="only time the canvas sampler (256 x 262144 bf16 logits per canvas)")
+    ap.add_argument("--selfcond", action="store_true",
+                    help="only time the self-conditioning input (256 x 262144 logits, d=2048, h=1920)")
     ap.add_argument("--decode", nargs="?", const="all", default=None, metavar="WORKLOAD",
                     help="only time decode attention (all workloads, or the one named: "
                          + ", ".join(DECODE_WORKLOADS) + ")")
@@ -581,11 +658,12 @@ def main():
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters,
-                           dtype="sampler" if args.sampler else "decode" if args.decode else args.dtype)
+                           dtype="sampler" if args.sampler else "decode" if args.decode
+                           else "selfcond" if args.selfcond else args.dtype)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, dtype=args.dtype, sampler=args.sampler,
-                        decode=args.decode)
+                        decode=args.decode, selfcond=args.selfcond)
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, dtype=args.dtype)
@@ -604,6 +682,9 @@ def main():
     torch.cuda.set_device(0)
     if args.sampler:
         print(json.dumps({"sampler": measure_sampler(max(args.steps, 10))}), flush=True)
+        return
+    if args.selfcond:
+        print(json.dumps({"selfcond": measure_selfcond(max(args.steps, 5))}), flush=True)
         return
     if args.decode:
         names = None if args.decode == "all" else [args.decode]
@@ -634,6 +715,7 @@ def main():
         result["fp8"] = fp8_summary()
         result["sampler"] = measure_sampler()
         result["decode"] = measure_decode()
+        result["selfcond"] = measure_selfcond()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline("cycle_l8k", args.cpu_seconds, args.dtype)
     print(json.dumps(result), flush=True)

@@ -555,8 +555,8 @@ static dg_status selfcond_layout(const dg_selfcond_shape* s, SelfcondLayout* l) 
   if (s->vocab < dg::kSelfcondBlock || s->vocab % dg::kSelfcondBlock != 0 ||
       s->vocab > DG_SELFCOND_MAX_VOCAB)
     return fail(DG_ERR_SHAPE, "vocab %d: a multiple of 32 in 32..%d", s->vocab, DG_SELFCOND_MAX_VOCAB);
-  if (s->d_model < 128 || s->d_model % 128 != 0 || s->d_model > 16384)
-    return fail(DG_ERR_SHAPE, "d_model %d: a multiple of 128 in 128..16384", s->d_model);
+  if (s->d_model < 256 || s->d_model % 256 != 0 || s->d_model > 16384)
+    return fail(DG_ERR_SHAPE, "d_model %d: a multiple of 256 in 256..16384", s->d_model);
   if (s->d_hidden < 128 || s->d_hidden % 128 != 0 || s->d_hidden > 16384)
     return fail(DG_ERR_SHAPE, "d_hidden %d: a multiple of 128 in 128..16384", s->d_hidden);
   const size_t M = (size_t)s->batch * DG_N_CANVAS;

@@ -17,7 +17,7 @@
 //   * gemm_kernel<DT>: C = A B for A blocked as above (M rows, 256 per tile) and
 //     B row-major [K][N] (the embedding table, W1, W2), split over K, fp32
 //     partials.  Eight waves as 4 row quarters x 2 column halves; 32-row stages
-//     stream HBM -> LDS with global_load_lds_dwordx4 through a ring of 4; A
+//     stream HBM -> LDS with global_load_lds_dwordx4 through a ring of 5; A
 //     operands by ds_read_b128, B operands by the transposing ds_read_b64_tr_b16
 //     (B is row-major in K, the matrix cores want K inside a lane); products on
 //     v_mfma_f32_32x32x16_bf16.  Units sharing an A tile (same rows and split,
@@ -41,7 +41,8 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kTK = kSelfcondBlock;  // contraction rows per stage = entries per block
 constexpr int kTileRows = 256;       // rows per product tile
-constexpr int kStages = 4;           // LDS ring of the product kernel
+constexpr int kStages = 5;           // LDS ring of the product kernel (160 KB at DT = 256)
+constexpr int kMaxSplits = 64;       // splits a reduce takes (the vocabulary limit keeps to it)
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -241,8 +242,9 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 16; i++) acc[rb][cb][i] = 0.f;
 
-  // ---- the ring: stage k in slot k mod 4; after the barrier of stage k every wave
-  //      is done with stage k-1, whose slot then takes stage k+3
+  // ---- the ring: stage k in slot k mod kStages; after the barrier of stage k every
+  //      wave is done with stage k-1, whose slot then takes stage k+kStages-1 (so
+  //      kStages-1 stages are in flight while one is computed)
 #pragma unroll
   for (int st = 0; st < kStages - 1; st++)
     if (st < nstages) issue(st, st);
@@ -307,42 +309,63 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return 0.5f * x * (1.f + t);
 }
 
+// Block (x, row): 256 threads, thread t sums columns 2048x + 8t .. +7 of the row over
+// the splits, eight splits' loads in flight at a time.  The split weights (softmax
+// merge: 2^(m_s - M) / sum_s 2^(m_s - M) l_s; otherwise 1) are formed once per
+// block by its first wave and shared through LDS.
 template <bool WEIGHTED, bool GELU, bool BLOCKED>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs r) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int N4 = r.N / 4;
-  if (idx >= (int64_t)r.M * N4) return;
-  const int row = (int)(idx / N4), c = 4 * (int)(idx % N4);
-  const int S = r.n_splits;
-  float mx = 0.f, den = 1.f;
-  if (WEIGHTED) {
-    mx = -1e30f;
-    for (int s = 0; s < S; s++) mx = fmaxf(mx, r.stats[(int64_t)s * r.M + row].x);
-    den = 0.f;
-    for (int s = 0; s < S; s++) {
-      const float2 st = r.stats[(int64_t)s * r.M + row];
-      den += __builtin_amdgcn_exp2f(st.x - mx) * st.y;
+  __shared__ float wsh[kMaxSplits];
+  const int row = blockIdx.y, S = r.n_splits;
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    float w = 0.f;
+    if (WEIGHTED) {
+      const float2 st = l < S ? r.stats[(int64_t)l * r.M + row] : make_float2(-1e30f, 0.f);
+      const float mx = wave_max(st.x);
+      w = l < S ? __builtin_amdgcn_exp2f(st.x - mx) : 0.f;
+      const float den = wave_sum(w * st.y);
+      w = den > 0.f ? w / den : 0.f;
+    } else {
+      w = 1.f;
+    }
+    if (l < S) wsh[l] = w;
+  }
+  __syncthreads();
+  const int c = 2048 * blockIdx.x + 8 * threadIdx.x;
+  if (c >= r.N) return;
+  const float* src = r.part + (int64_t)row * r.N + c;
+  const int64_t sstride = (int64_t)r.M * r.N;
+  // two float4 accumulators (a local array here ends up in scratch memory)
+  float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float4 v0[8], v1[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool ok = s0 + j < S;
+      v0[j] = ok ? *(const float4*)(src + (s0 + j) * sstride) : zero;
+      v1[j] = ok ? *(const float4*)(src + (s0 + j) * sstride + 4) : zero;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const float w = s0 + j < S ? wsh[s0 + j] : 0.f;
+      a0.x = fmaf(w, v0[j].x, a0.x);
+      a0.y = fmaf(w, v0[j].y, a0.y);
+      a0.z = fmaf(w, v0[j].z, a0.z);
+      a0.w = fmaf(w, v0[j].w, a0.w);
+      a1.x = fmaf(w, v1[j].x, a1.x);
+      a1.y = fmaf(w, v1[j].y, a1.y);
+      a1.z = fmaf(w, v1[j].z, a1.z);
+      a1.w = fmaf(w, v1[j].w, a1.w);
     }
   }
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < S; s++) {
-    const float4 v = *(const float4*)(r.part + ((int64_t)s * r.M + row) * r.N + c);
-    const float w = WEIGHTED ? __builtin_amdgcn_exp2f(r.stats[(int64_t)s * r.M + row].x - mx) : 1.f;
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
-  }
-  const float inv = WEIGHTED ? (den > 0.f ? 1.f / den : 0.f) : 1.f;
-  float o[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
-  if (GELU)
+  const float o[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  bf16x8 b;
 #pragma unroll
-    for (int e = 0; e < 4; e++) o[e] = gelu_tanh(o[e]);
-  bf16x4 b;
-#pragma unroll
-  for (int e = 0; e < 4; e++) b[e] = (__bf16)o[e];
+  for (int e = 0; e < 8; e++) b[e] = (__bf16)(GELU ? gelu_tanh(o[e]) : o[e]);
   const int64_t off = BLOCKED ? (((int64_t)(c >> 5) * r.M + row) << 5) + (c & 31) : (int64_t)row * r.N + c;
-  *(bf16x4*)((uint16_t*)r.out + off) = b;
+  *(bf16x8*)((uint16_t*)r.out + off) = b;
 }
 
 template <int DT>
@@ -354,14 +377,15 @@ int launch_gemm(const GemmArgs& g, hipStream_t st) {
 
 template <bool W, bool G, bool B>
 int launch_reduce(const ReduceArgs& r, hipStream_t st) {
-  const int64_t n = (int64_t)r.M * (r.N / 4);
-  hipLaunchKernelGGL((reduce_kernel<W, G, B>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, r);
+  hipLaunchKernelGGL((reduce_kernel<W, G, B>), dim3((r.N + 2047) / 2048, r.M), dim3(256), 0, st, r);
   return (int)hipGetLastError();
 }
 
-// one product plus its split sum
+// one product plus its split sum; the embedding product (mode 0) takes 256-wide
+// column tiles, the MLP's smaller products 128-wide ones (more units to spread)
 int product(const void* a, const void* b, int M, int N, int K, int split_k, float* part, const float2* stats,
             void* out, int mode, hipStream_t st, const SelfcondArgs& sa, int timed) {
+  const int dt = mode == 0 ? 256 : 128;
   GemmArgs g;
   g.a = a;
   g.b = b;
@@ -371,9 +395,9 @@ int product(const void* a, const void* b, int M, int N, int K, int split_k, floa
   g.K = K;
   g.split_k = split_k;
   g.n_splits = (K + split_k - 1) / split_k;
-  g.n_ntiles = N % 256 == 0 ? N / 256 : N / 128;
+  g.n_ntiles = N / dt;
   if (timed && sa.time_begin) sa.time_begin(0, st);
-  int err = N % 256 == 0 ? launch_gemm<256>(g, st) : launch_gemm<128>(g, st);
+  int err = dt == 256 ? launch_gemm<256>(g, st) : launch_gemm<128>(g, st);
   if (timed && sa.time_end) sa.time_end(0, st);
   if (err) return err;
   ReduceArgs r;
@@ -391,9 +415,10 @@ int product(const void* a, const void* b, int M, int N, int K, int split_k, floa
 }  // namespace
 
 int selfcond_splits(int K, int N, int M, int cus) {
-  // splits of the contraction so that the product units fill the device about once
-  const int tiles = (M / kTileRows) * (N % 256 == 0 ? N / 256 : N / 128);
-  int S = (cus + tiles - 1) / tiles;
+  // splits of an MLP product's contraction (128-wide column tiles) so that its
+  // units fill the device about once
+  const int tiles = (M / kTileRows) * (N / 128);
+  int S = min((cus + tiles - 1) / tiles, kMaxSplits);
   int sk = (K + S - 1) / S;
   sk = ((sk + kTK - 1) / kTK) * kTK;
   return sk;

@@ -269,7 +269,7 @@ typedef struct {
   int32_t batch;     /* B, 1..DG_MAX_BATCH                                        */
   int32_t n_canvas;  /* Nc, must equal DG_N_CANVAS                                */
   int32_t vocab;     /* V, a multiple of 32, 32..DG_SELFCOND_MAX_VOCAB            */
-  int32_t d_model;   /* d, a multiple of 128, 128..16384                          */
+  int32_t d_model;   /* d, a multiple of 256, 256..16384                          */
   int32_t d_hidden;  /* h, the MLP's hidden width, a multiple of 128, 128..16384  */
 } dg_selfcond_shape;
 

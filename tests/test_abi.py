@@ -243,7 +243,8 @@ def sc_shape(dg, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), -2), (dict(n_canvas=255), -2), (dict(vocab=100), -2), (dict(vocab=16), -2),
-    (dict(vocab=524288 + 32), -2), (dict(d_model=200), -2), (dict(d_hidden=0), -2),
+    (dict(vocab=524288 + 32), -2), (dict(d_model=200), -2), (dict(d_model=384), -2),
+    (dict(d_hidden=0), -2), (dict(d_hidden=200), -2),
 ])
 def test_selfcond_shape_errors(dg, kw, code):
     sh = sc_shape(dg, **kw)

@@ -53,8 +53,8 @@ def check(lg, E, w1, w2, rows=None):
 
 @pytest.mark.parametrize("B,V,d,h", [
     (1, 4096, 256, 128),          # one partial vocabulary split, 256-wide tiles
-    (2, 16384 + 96, 384, 256),    # ragged last split, 128-wide tiles, two row tiles
-    (1, 8192, 128, 384),
+    (2, 16384 + 96, 512, 384),    # ragged last split, two row tiles
+    (1, 8192, 256, 640),
 ])
 def test_selfcond_small(oracle_lib, B, V, d, h):
     err = check(*make(1400 + d, B, V, d, h))
