@@ -181,3 +181,23 @@ def test_decode_determinism(split_keys):
     a = gpu_decode(c)[0]
     b = gpu_decode(c)[0]
     np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("Hq,Hkv,k,L,forced", [
+    (32, 4, 16, [2500], 128),   # fp8, G = 8: four row tiles, splits of two chunks
+    (16, 8, 9, [0, 300], None),
+])
+def test_decode_fp8_gqa(oracle_lib, split_keys, Hq, Hkv, k, L, forced):
+    split_keys(forced)
+    c = make(1230 + k, len(L), L, k, Hq, Hkv, 128, "fp8")
+    got, kc_d, vc_d = gpu_decode(c)
+    ref = oracle_decode(oracle_lib, c)
+    ref_abs = oracle_decode(oracle_lib, c, absv=True)
+    # rows with fewer than 256 visible keys are outside the per-row statistical gate
+    fp8_check(got, ref, ref_abs, per_row=min(L) >= 256)
+    check_append(oracle_lib, c, kc_d, vc_d)
+
+
+def test_decode_bf16_d64_gqa4(oracle_lib, split_keys):
+    split_keys(64)
+    check_bf16(oracle_lib, make(1240, 2, [1500, 63], 16, 16, 4, 64, "bf16"))

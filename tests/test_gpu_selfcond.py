@@ -87,3 +87,19 @@ def test_selfcond_determinism():
     a = gpu(lg, E, w1, w2)
     b = gpu(lg, E, w1, w2)
     np.testing.assert_array_equal(a, b)
+
+
+def test_selfcond_largest_vocabulary(oracle_lib):
+    """V = 524288, the largest vocabulary the library takes: 64 vocabulary splits,
+    every one merged by the weighted split sum."""
+    V = 524288
+    lg, E, w1, w2 = make(1413, 1, V, 256, 128)
+    rows = np.array([0, 1, 77, 128, 200, 255])
+    err = check(lg, E, w1, w2, rows=rows)
+    print(f"selfcond V=524288: {err:.3e}")
+
+
+def test_selfcond_batch4(oracle_lib):
+    """Four canvases (1024 rows, four row tiles of the products)."""
+    err = check(*make(1414, 4, 8192, 256, 256))
+    print(f"selfcond B=4: {err:.3e}")
