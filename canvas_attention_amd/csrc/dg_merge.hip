@@ -116,12 +116,108 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
   }
 }
 
+// Decode calls (matrix-core kernels: bf16 partial rows, 32 rows per unit) have few
+// rows, Hq * n_q per sequence, and many splits: one thread per 8-element chunk would
+// walk the splits in a chain of dependent load batches.  Here the sum over splits
+// is spread over SG threads per chunk, each with all of its splits' loads in flight
+// (splits sg, sg + SG, ...), and the SG partial sums -- each a (max, weight sum,
+// weighted values) triple like a split's own -- are combined through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void merge_dec_kernel(AttnArgs a, Plan plan) {
+  constexpr int CPR = D / 8;       // 8-element chunks per row
+  constexpr int SG = 8;            // split groups per chunk
+  constexpr int IPB = 256 / SG;    // chunks per block
+  __shared__ float st[SG][IPB][10];
+  const int b = blockIdx.y;
+  const SeqPlan sp = plan.seq[b];
+  if (sp.n_splits == 1) return;  // written directly by the attention kernel
+  const int Hq = a.n_heads_q, G = plan.g, S = sp.n_splits, NRT = plan.n_rowtiles;
+  const int ti = threadIdx.x % IPB, sg = threadIdx.x / IPB;
+  const int item = blockIdx.x * IPB + ti;
+  const int rem = item / CPR, c8 = item % CPR;  // row of sequence b, chunk
+  const int M = plan.n_q * G;
+  const bool valid = rem < Hq * plan.n_q;
+  float mx = -1e30f, wsum = 0.f;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) o[e] = 0.f;
+  int g = 0, p = 0;
+  if (valid) {
+    g = div_rcp(rem, plan.rcp_m);
+    p = rem - g * M;
+    const int rt = p >> 5, pr = p & 31;
+    const int u0 = sp.unit_base + g * S * NRT + rt;
+    for (int s0 = sg; s0 < S; s0 += 8 * SG) {
+      float2 ml[8];
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int s = s0 + j * SG;
+        if (s < S) {
+          const int64_t base = (int64_t)(u0 + s * NRT) * 32 + pr;
+          ml[j] = *(const float2*)(a.part_ml + base * 2);
+          v[j] = *(const uint4*)((const uint16_t*)a.part_o + base * D + 8 * c8);
+        } else {
+          ml[j] = make_float2(-1e30f, 0.f);
+          v[j] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+      float mb = mx;
+#pragma unroll
+      for (int j = 0; j < 8; j++) mb = fmaxf(mb, ml[j].x);
+      const float r = exp2f(mx - mb);
+#pragma unroll
+      for (int e = 0; e < 8; e++) o[e] *= r;
+      wsum *= r;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const float w = exp2f(ml[j].x - mb) * ml[j].y;
+        const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          o[e] = fmaf(w, __uint_as_float((e & 1) ? (wd[e / 2] & 0xffff0000u) : (wd[e / 2] << 16)), o[e]);
+        wsum += w;
+      }
+      mx = mb;
+    }
+  }
+  st[sg][ti][0] = mx;
+  st[sg][ti][1] = wsum;
+#pragma unroll
+  for (int e = 0; e < 8; e++) st[sg][ti][2 + e] = o[e];
+  __syncthreads();
+  if (sg != 0 || !valid) return;
+  float M2 = -1e30f;
+#pragma unroll
+  for (int k = 0; k < SG; k++) M2 = fmaxf(M2, st[k][ti][0]);
+  float W = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) acc[e] = 0.f;
+#pragma unroll
+  for (int k = 0; k < SG; k++) {
+    const float f = exp2f(st[k][ti][0] - M2);
+    W += f * st[k][ti][1];
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[e] = fmaf(f, st[k][ti][2 + e], acc[e]);
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  const int i = div_rcp(p, plan.rcp_g), hh = p - i * G;
+  typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+  bf16x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; e++) out[e] = (__bf16)(acc[e] * inv);
+  *(bf16x8*)((uint16_t*)a.out + ((int64_t)(b * plan.n_q + i) * Hq + g * G + hh) * D + 8 * c8) = out;
+}
+
 template <int D, bool BF16OUT>
 int launch_t(const AttnArgs& a, const Plan& p, hipStream_t st) {
   constexpr int RPB = 256 / (D / (BF16OUT ? 8 : 4));
   const int rows = a.n_heads_q * p.n_q;  // per sequence
   const dim3 grid((rows + RPB - 1) / RPB, p.batch);
-  if (p.n_q == kCanvas)
+  if (p.n_q != kCanvas && BF16OUT && p.rows_per_unit == 32) {  // matrix-core decode
+    const int chunks = rows * (D / 8);
+    hipLaunchKernelGGL((merge_dec_kernel<D>), dim3((chunks + 31) / 32, p.batch), dim3(256), 0, st, a, p);
+  } else if (p.n_q == kCanvas)
     hipLaunchKernelGGL((merge_kernel<D, BF16OUT, false>), grid, dim3(256), 0, st, a, p);
   else
     hipLaunchKernelGGL((merge_kernel<D, BF16OUT, true>), grid, dim3(256), 0, st, a, p);
