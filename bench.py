@@ -463,6 +463,23 @@ def fp8_summary(reps=100):
             "kernel": "attn_fp8_kernel<128,false>", "timing": f"median of {reps} calls, warm"}
 
 
+def back_to_back(call, reps, stream):
+    """Milliseconds of each of `reps` calls enqueued back to back, one pair of events
+    around each, one synchronisation at the end (a wait per call would add the
+    host's launch latency to every interval)."""
+    import torch
+    evs = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def measure_sampler(reps=50, batch=1):
     """The canvas sampler (dg_canvas_sample) on one step's logits: B canvases of
     256 positions over the 262144-token vocabulary, tau 0.8 (the start of the
@@ -477,16 +494,8 @@ def measure_sampler(reps=50, batch=1):
     for _ in range(5):
         dg.canvas_sample(lg, nz, None, 0.8, 0.1, 0.005)
     torch.cuda.synchronize()
-    ts = []
     stream = torch.cuda.current_stream()
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        dg.canvas_sample(lg, nz, None, 0.8, 0.1, 0.005)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
+    ts = back_to_back(lambda: dg.canvas_sample(lg, nz, None, 0.8, 0.1, 0.005), reps, stream)
     us = float(np.median(ts)) * 1e3
     nbytes = batch * 256 * synth.VOCAB * 2
     return {"batch": batch, "vocab": synth.VOCAB, "call_us_median": round(us, 3),
@@ -547,18 +556,13 @@ def measure_decode(reps=50, names=None):
             dg.kernel_timing_enable(False)
             # ... and the whole call (kernel + merge when there is one), one pair of
             # events around it, without the per-launch events
-            evs = []
-            for i in range(reps):
-                if mode == "cold":
+            if mode == "cold":
+                c_ms = []
+                for _ in range(reps):  # the flush stays outside the timed interval
                     flush()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                call()
-                e1.record(stream)
-                evs.append((e0, e1))
-            torch.cuda.synchronize()
-            c_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+                    c_ms += back_to_back(call, 1, stream)
+            else:
+                c_ms = back_to_back(call, reps, stream)
             med[mode] = {"kernel": round(float(np.median(a_ms)) * 1e3, 3),
                          "call": round(float(np.median(c_ms)) * 1e3, 3)}
         nbytes = decode_bytes(B, Lv, k, Hq, Hkv, D)
@@ -608,15 +612,7 @@ def measure_selfcond(reps=20):
         call()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ts = []
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        call()
-        b.record(stream)
-        torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
+    ts = back_to_back(call, reps, stream)
     dg.kernel_timing_read()
     dg.kernel_timing_enable(True)
     for _ in range(reps):
