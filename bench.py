@@ -450,6 +450,42 @@ def measure(dtype, steps, warmup, profile_steps=False):
     }
 
 
+def long_context_summary(reps=20):
+    """The canvas step of the long-context workload (B=1, L=131072, Hq=16, Hkv=8,
+    D=128, bf16): median per call of the attention kernel (the library's events)
+    and of attention + merge, warm, with the kernel's fraction of the bf16 MFMA
+    peak -- the same kernel as the headline step, with 16x the keys per unit, so
+    its fixed costs weigh less."""
+    import torch
+    import canvas_attention_amd.dg as dg
+    from canvas_attention_amd import synth
+    w = synth.WORKLOADS["long_l128k"]
+    B, Hq, Hkv, D, seed = w["batch"], w["hq"], w["hkv"], w["d"], w["seed"]
+    L = synth.prefix_lengths("long_l128k")
+    Lv = int(L[0])
+    kc, vc = (dev(x) for x in synth.cache(seed, L, Lv, Hkv, D, "bf16"))
+    q, kn, vn = (dev(x) for x in synth.canvas(seed, B, Hq, Hkv, D, "bf16"))
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    ws = dg.alloc_workspace(q, Hkv, Lv)
+    for _ in range(3):
+        dg.canvas_attn(q, kc, vc, L, kn, vn, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    dg.kernel_timing_read()
+    dg.kernel_timing_enable(True)
+    for _ in range(reps):
+        dg.canvas_attn(q, kc, vc, L, kn, vn, out=out, workspace=ws)
+    a_ms, m_ms = dg.kernel_timing_samples(reps)
+    dg.kernel_timing_enable(False)
+    attn_us = float(np.median(a_ms)) * 1e3
+    step_us = float(np.median(np.add(a_ms, m_ms if len(m_ms) == len(a_ms) else 0.0))) * 1e3
+    fl = step_flops(B, Hq, Lv, D)
+    del kc, vc
+    return {"prefix_len": Lv, "canvas_attn_us": round(attn_us, 2), "canvas_step_us": round(step_us, 2),
+            "canvas_attn_tflops": round(fl / (attn_us * 1e-6) / 1e12, 1),
+            "frac_of_bf16_peak": round(fl / (attn_us * 1e-6) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+            "kernel": "attn_bf16_kernel<128,false>", "timing": f"median of {reps} calls, warm"}
+
+
 def fp8_summary(reps=100):
     """The fp8 canvas step at L=8192 (warm median per call) for the bf16 line."""
     cy = Cycle("fp8")
@@ -648,6 +684,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sampler", action="store_true",
                     help="only time the canvas sampler (256 x 262144 bf16 logits per canvas)")
+    ap.add_argument("--long-context", action="store_true",
+                    help="only time the L=131072 canvas step")
     ap.add_argument("--selfcond", action="store_true",
                     help="only time the self-conditioning input (256 x 262144 logits, d=2048, h=1920)")
     ap.add_argument("--decode", nargs="?", const="all", default=None, metavar="WORKLOAD",
@@ -697,6 +735,9 @@ def main():
     if args.selfcond:
         print(json.dumps({"selfcond": measure_selfcond(max(args.steps, 5))}), flush=True)
         return
+    if args.long_context:
+        print(json.dumps({"long_context": long_context_summary(max(args.steps, 5))}), flush=True)
+        return
     if args.decode:
         names = None if args.decode == "all" else [args.decode]
         print(json.dumps({"decode": measure_decode(max(args.steps, 10), names)}), flush=True)
@@ -724,6 +765,7 @@ def main():
     }
     if args.dtype == "bf16":
         result["fp8"] = fp8_summary()
+        result["long_context"] = long_context_summary()
         result["sampler"] = measure_sampler()
         result["decode"] = measure_decode()
         result["selfcond"] = measure_selfcond()
