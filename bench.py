@@ -479,10 +479,12 @@ def long_context_summary(reps=20):
     attn_us = float(np.median(a_ms)) * 1e3
     step_us = float(np.median(np.add(a_ms, m_ms if len(m_ms) == len(a_ms) else 0.0))) * 1e3
     fl = step_flops(B, Hq, Lv, D)
+    gbs = step_bytes(B, Hq, Hkv, Lv, D) / (attn_us * 1e-6) / 1e9
     del kc, vc
     return {"prefix_len": Lv, "canvas_attn_us": round(attn_us, 2), "canvas_step_us": round(step_us, 2),
             "canvas_attn_tflops": round(fl / (attn_us * 1e-6) / 1e12, 1),
             "frac_of_bf16_peak": round(fl / (attn_us * 1e-6) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+            "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
             "kernel": "attn_bf16_kernel<128,false>", "timing": f"median of {reps} calls, warm"}
 
 
