@@ -201,3 +201,34 @@ def test_decode_fp8_gqa(oracle_lib, split_keys, Hq, Hkv, k, L, forced):
 def test_decode_bf16_d64_gqa4(oracle_lib, split_keys):
     split_keys(64)
     check_bf16(oracle_lib, make(1240, 2, [1500, 63], 16, 16, 4, 64, "bf16"))
+
+
+def test_decode_shared_workspace(oracle_lib, split_keys):
+    """One workspace, sized for the largest of the calls, serves a run of decode calls
+    of different token counts, prefixes, split sizes and element types, each checked
+    against the oracle (nothing of one call's partials leaks into the next)."""
+    split_keys(None)
+    Hq, Hkv, D = 16, 8, 128
+    cases = [(1251, [8192], 1, "bf16", None), (1252, [8192], 16, "bf16", None),
+             (1253, [40000], 1, "bf16", None), (1254, [8192], 1, "fp8", None),
+             (1255, [3000], 2, "bf16", 64), (1256, [8192], 1, "bf16", None)]
+    tdt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+    n = 0
+    for _, L, k, dt, forced in cases:  # the forced split size is part of the size query
+        split_keys(forced)
+        n = max(n, dg.decode_workspace_bytes(1, k, Hq, Hkv, D, L[0], tdt[dt]))
+    ws = torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda")
+    for seed, L, k, dt, forced in cases:
+        split_keys(forced)
+        c = make(seed, 1, L, k, Hq, Hkv, D, dt)
+        kc_d, vc_d = to_dev(c["kc"]), to_dev(c["vc"])
+        out = dg.decode_attn(to_dev(c["q"]), to_dev(c["kn"]), to_dev(c["vn"]), kc_d, vc_d, c["L"],
+                             workspace=ws)
+        torch.cuda.synchronize()
+        got, ref = to_host_f64(out), oracle_decode(oracle_lib, c)
+        if dt == "bf16":
+            err = row_err(got, ref)
+            assert err <= TOL_BF16, f"seed {seed}: per-row error {err:.3e}"
+        else:
+            fp8_check(got, ref, oracle_decode(oracle_lib, c, absv=True), per_row=True)
+        check_append(oracle_lib, c, kc_d, vc_d)
