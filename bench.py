@@ -45,19 +45,21 @@ ELEM_BYTES = {"bf16": 2, "fp8": 1}
 # profile files of its counter summaries
 ATTN_KERNELS = {"bf16": "attn_bf16_kernel<128, false", "fp8": "attn_fp8_kernel<128, false",
                 "sampler": "row_stats_kernel", "decode": "decode_kernel<dg::(anonymous namespace)::FmtBf16, 128",
-                "selfcond": "gemm_kernel<256>"}
+                "selfcond": "gemm_kernel<256>", "long": "attn_bf16_kernel<128, false"}
 PROFILE_TAG = {"bf16": "canvas_attn_l8k", "fp8": "canvas_attn_fp8_l8k", "sampler": "canvas_sample_v262k",
-               "decode": "decode_attn_b32_l8k", "selfcond": "selfcond_v262k_d2048"}
+               "decode": "decode_attn_b32_l8k", "selfcond": "selfcond_v262k_d2048",
+               "long": "canvas_attn_l128k"}
 PROFILE_WHAT = {"bf16": "the canvas attention kernel (bf16; canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)",
                 "fp8": "the canvas attention kernel (fp8; canvas step, L=8192, B=1, Hq=16, Hkv=8, D=128)",
                 "sampler": "the sampler's row statistics kernel (B=1, 256 positions, V=262144 bf16 logits)",
                 "decode": "the decode attention kernel (bf16; 32 sequences at L=8192, one new token each, "
                           "Hq=16, Hkv=8, D=128)",
                 "selfcond": "the self-conditioning embedding product (256 x 262144 softmax weights times "
-                            "E [262144 x 2048], bf16)"}
+                            "E [262144 x 2048], bf16)",
+                "long": "the canvas attention kernel (bf16; canvas step, L=131072, B=1, Hq=16, Hkv=8, D=128)"}
 PROFILE_RUN = {"bf16": "--steps 2 --warmup 1 --profile-steps", "fp8": "--steps 2 --warmup 1 --profile-steps --dtype fp8",
                "sampler": "--sampler --steps 10", "decode": "--decode b32_l8k_k1 --steps 10",
-               "selfcond": "--selfcond --steps 10"}
+               "selfcond": "--selfcond --steps 10", "long": "--long-context --steps 5"}
 
 # Decode attention workloads (AR mode over the same cache; the concurrency
 # crossover of the pages sits near 32 sequences): Hq=16, Hkv=8, D=128, bf16.
@@ -150,7 +152,7 @@ def _counter_per_dispatch(folder, counter, name_part):
 def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, dtype="bf16"):
     ATTN_KERNEL = ATTN_KERNELS[dtype]
     flag = {"bf16": "", "fp8": " --dtype fp8", "sampler": " --sampler", "decode": " --decode",
-            "selfcond": " --selfcond"}[dtype]
+            "selfcond": " --selfcond", "long": " --long-context"}[dtype]
     copy_bytes = int(copy_mib) * (1 << 20)
     f_kib, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", ATTN_KERNEL)
     w_kib, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", ATTN_KERNEL)
@@ -241,7 +243,8 @@ def summarize_mfma(pass1_dir, pass2_dir, trace_txt, dtype="bf16"):
     print(open(out).read())
 
 
-def summarize_trace(stats_csv, out_txt, dtype="bf16", sampler=False, decode=None, selfcond=False):
+def summarize_trace(stats_csv, out_txt, dtype="bf16", sampler=False, decode=None, selfcond=False,
+                    long_context=False):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     keep = [r for r in rows if "dg::" in r["Name"] or "copyBuffer" in r["Name"]]
@@ -253,6 +256,9 @@ def summarize_trace(stats_csv, out_txt, dtype="bf16", sampler=False, decode=None
     if selfcond:
         run = "--selfcond --steps 20"
         flag = " --selfcond"
+    if long_context:
+        run = "--long-context --steps 10"
+        flag = " --long-context"
     lines = ["# rocprofv3 --kernel-trace --stats summary (kernels of this library)",
              "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              f"-d <dir> -o run -- python3 <repo>/bench.py {run}",
@@ -479,12 +485,16 @@ def long_context_summary(reps=20):
     attn_us = float(np.median(a_ms)) * 1e3
     step_us = float(np.median(np.add(a_ms, m_ms if len(m_ms) == len(a_ms) else 0.0))) * 1e3
     fl = step_flops(B, Hq, Lv, D)
-    gbs = step_bytes(B, Hq, Hkv, Lv, D) / (attn_us * 1e-6) / 1e9
+    alg = step_bytes(B, Hq, Hkv, Lv, D)
+    gbs = alg / (attn_us * 1e-6) / 1e9
     del kc, vc
     return {"prefix_len": Lv, "canvas_attn_us": round(attn_us, 2), "canvas_step_us": round(step_us, 2),
             "canvas_attn_tflops": round(fl / (attn_us * 1e-6) / 1e12, 1),
             "frac_of_bf16_peak": round(fl / (attn_us * 1e-6) / 1e12 / PEAK_TFLOPS["bf16"], 4),
             "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes_per_launch": int(alg),
+            # FETCH_SIZE + WRITE_SIZE per launch (calibrated counters), while they match the kernel
+            "traffic": measured_traffic("long"),
             "kernel": "attn_bf16_kernel<128,false>", "timing": f"median of {reps} calls, warm"}
 
 
@@ -710,11 +720,12 @@ def main():
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters,
                            dtype="sampler" if args.sampler else "decode" if args.decode
-                           else "selfcond" if args.selfcond else args.dtype)
+                           else "selfcond" if args.selfcond else "long" if args.long_context
+                           else args.dtype)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, dtype=args.dtype, sampler=args.sampler,
-                        decode=args.decode, selfcond=args.selfcond)
+                        decode=args.decode, selfcond=args.selfcond, long_context=args.long_context)
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, dtype=args.dtype)
