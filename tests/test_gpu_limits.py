@@ -1,5 +1,6 @@
 """GPU parity at the library's largest batch (DG_MAX_BATCH sequences) and, for
-decode, the largest token count (DG_MAX_DECODE), against the CPU fp64 oracle.
+decode, the largest token count (DG_MAX_DECODE), and on caches whose addresses
+pass 2^32 bytes, against the CPU fp64 oracle.
 
 Prefix lengths are ragged and include the degenerate ones: an empty cache, a
 single row, and lengths on and just off the 32-key chunk boundary.  Every output
@@ -107,3 +108,50 @@ def test_fp8_canvas_step_max_batch(oracle_lib):
     absv = (lambda x: x & np.uint8(0x7F))
     ref_abs = oracle_lib.canvas_attn(q, kc, absv(vc), L, kn, absv(vn))
     fp8_check(to_host_f64(out), ref, ref_abs, per_row=True)
+
+
+def test_cache_beyond_4gib(oracle_lib):
+    """Caches of 2^21 rows (8 kv heads x 128 bf16): sequence 1 starts 4 GiB into each
+    cache tensor, so its addresses lie past 2^32 bytes, in the canvas step, the commit
+    with its append and a decode call after it.  Rows past the oracle's capacity are
+    left uninitialised on the device: no kernel may read them."""
+    B, Hq, Hkv, D, cap = 2, 16, 8, 128, 1 << 21
+    L = np.array([700, 1234], np.int32)
+    small = int(L.max()) + 256 + 16
+    kc, vc = synth.cache(1306, L, small, Hkv, D, "bf16")
+    big = []
+    for a in (kc, vc):
+        t = torch.empty((B, cap, Hkv, D), dtype=torch.bfloat16, device="cuda")
+        t[:, :small] = to_dev(a)
+        big.append(t)
+    kc_d, vc_d = big
+
+    def cached(t):
+        return to_host_bits(t[:, :small].contiguous())
+
+    q, kn, vn = synth.canvas(1306, B, Hq, Hkv, D, "bf16")
+    out = dg.canvas_attn(to_dev(q), kc_d, vc_d, L, to_dev(kn), to_dev(vn))
+    torch.cuda.synchronize()
+    err = row_err(to_host_f64(out), oracle_lib.canvas_attn(q, kc, vc, L, kn, vn))
+    assert err <= TOL_BF16, f"canvas step: per-row error {err:.3e}"
+
+    qb, kb, vb = synth.block(1306, B, Hq, Hkv, D, "bf16")
+    outc = dg.commit_block(to_dev(qb), to_dev(kb), to_dev(vb), kc_d, vc_d, L)
+    torch.cuda.synchronize()
+    err = row_err(to_host_f64(outc), oracle_lib.commit_attn(qb, kc, vc, L, kb, vb))
+    assert err <= TOL_BF16, f"commit: per-row error {err:.3e}"
+    oracle_lib.append_block(kb, vb, kc, vc, L)
+    np.testing.assert_array_equal(cached(kc_d), kc)
+    np.testing.assert_array_equal(cached(vc_d), vc)
+
+    L2 = L + 256
+    qd, knd, vnd = synth.decode(1306, B, 4, Hq, Hkv, D, "bf16")
+    outd = dg.decode_attn(to_dev(qd), to_dev(knd), to_dev(vnd), kc_d, vc_d, L2)
+    torch.cuda.synchronize()
+    err = row_err(to_host_f64(outd), oracle_lib.decode_attn(qd, kc, vc, L2, knd, vnd))
+    assert err <= TOL_BF16, f"decode: per-row error {err:.3e}"
+    oracle_lib.append_block(knd, vnd, kc, vc, L2)
+    np.testing.assert_array_equal(cached(kc_d), kc)
+    np.testing.assert_array_equal(cached(vc_d), vc)
+    del kc_d, vc_d, big
+    torch.cuda.empty_cache()
