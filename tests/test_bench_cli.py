@@ -24,3 +24,21 @@ def test_algorithmic_counts():
     # decode bytes: the cache K and V of the prefix dominate
     b = bench.decode_bytes(32, 8192, 1, 16, 8, 128)
     assert 2 * 32 * 8192 * 8 * 128 * 2 < b < 1.001 * 2 * 32 * 8192 * 8 * 128 * 2
+
+
+def test_counted_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
+    """A counter file is reported only while its hash matches the kernel source it
+    was taken on; a missing file or another hash gives null traffic."""
+    import bench
+    tag = "canvas_attn_l128k"
+    good = "\n".join(["# counters", f"kernel_source_hash: {bench.kernel_source_hash('long')}",
+                      "traffic_bytes_per_launch: 547886180"]) + "\n"
+    stale = good.replace(bench.kernel_source_hash("long"), "0000000000000000")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("long") is None
+    (prof / f"{tag}_traffic.txt").write_text(good)
+    assert bench.measured_traffic("long") == 547886180
+    (prof / f"{tag}_traffic.txt").write_text(stale)
+    assert bench.measured_traffic("long") is None
