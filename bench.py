@@ -6,12 +6,17 @@ causal commit of the block with its cache append (dg_commit_block), batch 1,
 Hq=16, Hkv=8, head_dim=128, bf16 storage with fp32 accumulation (--dtype fp8:
 OCP e4m3 storage with tensor scales 1, fp32 accumulation, bf16 output).
 
-Prints one JSON line.  value = algorithmic TFLOP/s of the whole cycle
-(canvas step 4*B*Hq*256*(L+256)*D, commit 4*B*Hq*D*(256*L + 256*257/2), exp
-and max not counted).  The roofline object is for the dominant kernel (the
-split-key canvas attention kernel), timed with HIP events that the library
-records on its launch stream.  cpu_baseline times the CPU fp64 oracle on a
-bounded sample of the same workload.  The default (bf16) line also carries the
+Prints one JSON line.  value = algorithmic TFLOP/s of the canvas step (the
+metric's quantity: 4*B*Hq*256*(L+256)*D per step, exp and max not counted),
+taken from the timed block cycles themselves: an event pair brackets the 12
+steps of every cycle, so the step time holds attention and merge.  Beside it:
+canvas positions per second, the fraction of the bf16 MFMA peak, and the whole
+cycle's TFLOP/s (commit: 4*B*Hq*D*(256*L + 256*257/2)).  ms_per_step is the
+block cycle.  The roofline object is for the dominant kernel (the split-key
+canvas attention kernel), timed with HIP events that the library records on
+its launch stream.  cpu_baseline times the CPU fp64 oracle on bounded samples
+of the L=2048, L=8192 and L=131072 canvas steps, on all host threads and on
+one.  The default (bf16) line also carries the
 fp8 canvas step's kernel time and its fraction of the fp8 MFMA peak, the
 canvas sampler's time per call over one step's logits (--sampler: only that),
 decode attention (AR mode, 1 or 16 new tokens over the same cache) on four
@@ -81,8 +86,10 @@ def traffic_file(dtype):
 # (FETCH_SIZE and WRITE_SIZE per dispatch, calibrated against a plain copy of
 # known size) recorded in a profile file together with a hash of the kernel
 # source; it is reported only while the source still matches.
+# The attention kernels' counted traffic also depends on the split plan (dg_api.cpp
+# sets how many partial rows a launch writes) and on the merge that reads them.
 KERNEL_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
-                  for f in ("dg_attn_mfma.hip", "dg_internal.h")]
+                  for f in ("dg_attn_mfma.hip", "dg_internal.h", "dg_api.cpp", "dg_merge.hip")]
 SAMPLER_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
                    for f in ("dg_sample.hip", "dg_internal.h")]
 SELFCOND_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
@@ -259,7 +266,10 @@ def summarize_trace(stats_csv, out_txt, dtype="bf16", sampler=False, decode=None
     if long_context:
         run = "--long-context --steps 10"
         flag = " --long-context"
+    tag = ("sampler" if sampler else "decode" if decode else "selfcond" if selfcond
+           else "long" if long_context else dtype)
     lines = ["# rocprofv3 --kernel-trace --stats summary (kernels of this library)",
+             f"# kernel_source_hash: {kernel_source_hash(tag)}",
              "# command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              f"-d <dir> -o run -- python3 <repo>/bench.py {run}",
              "# (written by: python3 bench.py --summarize-trace <dir>/run_kernel_stats.csv OUT"
@@ -389,16 +399,21 @@ def measure(dtype, steps, warmup, profile_steps=False):
     for _ in range(warmup):
         cycle()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
-        cycle()
-    t1.record(stream)
+    # the timed region: `steps` block cycles back to back; within it one more
+    # event after each cycle's 12 canvas steps splits steps from commit
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        cy.steps()
+        evs[2 * i + 1].record(stream)
+        cy.commit()
+        evs[2 * i + 2].record(stream)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    ms = evs[0].elapsed_time(evs[-1]) / steps
     if profile_steps:
         return {"ms_per_step": ms}
+    steps_ms = sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(steps))
+    step_ms = steps_ms / (steps * n_steps)
 
     fl_step = step_flops(B, Hq, Lv, D)
     fl_commit = commit_flops(B, Hq, Lv, D)
@@ -420,21 +435,14 @@ def measure(dtype, steps, warmup, profile_steps=False):
     merge_us = merge_ms / max(n_merge, 1) * 1e3 if n_merge else 0.0
     achieved = fl_step / (attn_us * 1e-6) / 1e12
 
-    # canvas steps alone (whole step incl. merge), for positions/s
-    t0.record(stream)
-    for _ in range(steps):
-        cy.steps()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / (steps * n_steps)
     reps = max(steps, 50)
     medians = call_medians(cy, reps)
     kname = ATTN_KERNELS[dtype].replace(", ", ",")
     return {
-        "value": round(fl_cycle / (ms * 1e-3) / 1e12, 2),
+        "value": round(fl_step / (step_ms * 1e-3) / 1e12, 2),
         "ms_per_step": round(ms, 5),
+        "block_cycle_tflops": round(fl_cycle / (ms * 1e-3) / 1e12, 2),
         "canvas_step_us": round(step_ms * 1e3, 3),
-        "canvas_step_tflops": round(fl_step / (step_ms * 1e-3) / 1e12, 2),
         "canvas_positions_per_s": round(B * 256 / (step_ms * 1e-3), 1),
         "canvas_step_mfma_frac": round(fl_step / (step_ms * 1e-3) / 1e12 / peak, 4),
         "canvas_call_us_median": {"warm": medians["warm"], "cold": medians["cold"],
@@ -703,7 +711,7 @@ def main():
     ap.add_argument("--decode", nargs="?", const="all", default=None, metavar="WORKLOAD",
                     help="only time decode attention (all workloads, or the one named: "
                          + ", ".join(DECODE_WORKLOADS) + ")")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only run the timed cycles (for rocprofv3 runs)")
@@ -773,7 +781,8 @@ def main():
         "vs_baseline": None,
         "dtype": args.dtype,
         "data": "synthetic",
-        "config": {"workload": "block cycle: 12 canvas steps + commit at prefix L=8192", **cfg},
+        "config": {"workload": "canvas denoising step at prefix L=8192 (timed inside block cycles of "
+                               "12 canvas steps + commit; ms_per_step is one cycle)", **cfg},
         **m,
     }
     if args.dtype == "bf16":
@@ -783,36 +792,52 @@ def main():
         result["decode"] = measure_decode()
         result["selfcond"] = measure_selfcond()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline("cycle_l8k", args.cpu_seconds, args.dtype)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, args.dtype)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(name, budget_s, dtype="bf16"):
-    """The CPU fp64 oracle on a bounded sample of the same workload: whole canvas
-    steps of the block cycle (each with its own seeded canvas Q/K/V, all 256
-    positions and all heads), one after another until the time budget is spent."""
+def cpu_baseline(budget_s, dtype="bf16"):
+    """The CPU fp64 oracle (as it stands, untuned) on bounded samples of the canvas
+    step at L=2048, L=8192 and L=131072 (B=1, 256 positions, Hq=16, Hkv=8, D=128):
+    whole steps, each with its own seeded canvas Q/K/V, one after another until a
+    share of the time budget is spent (at least one step), on all the threads the
+    oracle's OpenMP runtime takes; then the L=2048 and L=8192 steps on one thread.
+    value is the L=8192 figure on all threads (the metric's workload)."""
     import oracle
     from canvas_attention_amd import synth
-    w = synth.WORKLOADS[name]
-    B, Hq, Hkv, D, seed = w["batch"], w["hq"], w["hkv"], w["d"], w["seed"]
-    L = synth.prefix_lengths(name)
-    Lv = int(L[0])
-    kc, vc = synth.cache(seed, L, Lv + 256, Hkv, D, dtype)
-    steps = [synth.canvas(seed, B, Hq, Hkv, D, dtype, step=s) for s in range(w["steps"])]
-    done = 0
-    t_start = time.perf_counter()
-    elapsed = 0.0
-    while elapsed < budget_s:
-        q, kn, vn = steps[done % len(steps)]
-        oracle.canvas_attn(q, kc, vc, L, kn, vn)
-        done += 1
-        elapsed = time.perf_counter() - t_start
-    flops = done * step_flops(B, Hq, Lv, D)
-    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{done} whole canvas steps of the L={Lv} block cycle (B={B}, 256 "
-                      f"positions, Hq={Hq}, Hkv={Hkv}, D={D}) in {elapsed:.1f} s: "
-                      f"{done * B * 256 / elapsed:.1f} canvas positions/s"}
+    threads = oracle.num_threads()
+    shares = {"step_l2k": 0.15, "cycle_l8k": 0.25, "long_l128k": 0.0}
+    one_thread = {"step_l2k": 0.1, "cycle_l8k": 0.35}
+
+    def run(name, budget, nthreads):
+        w = synth.WORKLOADS[name]
+        B, Hq, Hkv, D, seed = w["batch"], w["hq"], w["hkv"], w["d"], w["seed"]
+        L = synth.prefix_lengths(name)
+        Lv = int(L[0])
+        kc, vc = synth.cache(seed, L, Lv + 256, Hkv, D, dtype)
+        steps = [synth.canvas(seed, B, Hq, Hkv, D, dtype, step=s) for s in range(3)]
+        oracle.set_num_threads(nthreads)
+        done, t_start, elapsed = 0, time.perf_counter(), 0.0
+        while done == 0 or elapsed < budget:
+            q, kn, vn = steps[done % len(steps)]
+            oracle.canvas_attn(q, kc, vc, L, kn, vn)
+            done += 1
+            elapsed = time.perf_counter() - t_start
+        fl = done * step_flops(B, Hq, Lv, D)
+        return {"prefix_len": Lv, "threads": nthreads, "steps": done, "seconds": round(elapsed, 2),
+                "TFLOP/s": round(fl / elapsed / 1e12, 6),
+                "canvas_positions_per_s": round(done * B * 256 / elapsed, 1)}
+
+    figs = {f"{n}_all_threads": run(n, budget_s * f, threads) for n, f in shares.items()}
+    figs.update({f"{n}_1_thread": run(n, budget_s * f, 1) for n, f in one_thread.items()})
+    oracle.set_num_threads(threads)
+    main = figs["cycle_l8k_all_threads"]
+    return {"value": main["TFLOP/s"], "unit": "TFLOP/s", "cores": threads,
+            "cpu_count": os.cpu_count(), "kind": "oracle",
+            "sample": f"{main['steps']} whole canvas steps at L=8192 (B=1, 256 positions, Hq=16, Hkv=8, "
+                      f"D=128) on {threads} threads in {main['seconds']} s: "
+                      f"{main['canvas_positions_per_s']} canvas positions/s; baseline only",
+            "configs": figs}
 
 
 if __name__ == "__main__":

@@ -64,22 +64,7 @@ bool mfma_path(int dtype) { return dtype != DG_F32; }
 // Keys per chunk of the kernel a dtype runs on: split boundaries are multiples of it.
 int key_granule(int dtype) { return dtype == DG_FP8 ? 64 : dg::kKeyGranule; }
 
-// bf16 kernel shape for a call: DG_VARIANT=0..2 forces one for head_dim 128
-// (for tuning); otherwise the default shape.  head_dim 64 has one shape.
-int bf16_variant(int head_dim) {
-  if (head_dim != 128) return dg::kDefaultVariant;
-  const char* e = getenv("DG_VARIANT");
-  if (e && *e) {
-    const long v = strtol(e, nullptr, 10);
-    if (v >= 0 && v < dg::kNumVariants) return (int)v;
-  }
-  return dg::kDefaultVariant;
-}
-
-int rows_per_unit(int dtype, int variant) {
-  if (dtype == DG_FP8) return dg::variant_rows(dg::kVariantR128);
-  return dtype == DG_BF16 ? dg::variant_rows(variant) : dg::kRowsF32;
-}
+int rows_per_unit(int dtype) { return mfma_path(dtype) ? dg::kRowsMfma : dg::kRowsF32; }
 
 // Call kinds: the canvas step, the block commit and decode attention.
 enum Mode { kCanvasStep = 0, kCommit = 1, kDecode = 2 };
@@ -141,8 +126,7 @@ int target_units(int dtype) { return device_cu_count() * (mfma_path(dtype) ? 1 :
 // Split-key plan: every unit of every sequence gets about the same number of
 // keys, chosen so that the units fill the device about once.
 void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
-  const int variant = s->dtype == DG_FP8 ? dg::kVariantR128 : bf16_variant(s->head_dim);
-  const int R = rows_per_unit(s->dtype, variant);
+  const int R = rows_per_unit(s->dtype);
   const int G = s->n_heads_q / s->n_heads_kv;
   const int NRT = dg::kCanvas * G / R;
   const int per_split = s->n_heads_kv * NRT;  // units per split index
@@ -159,7 +143,6 @@ void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
   p->batch = s->batch;
   p->n_q = dg::kCanvas;
   p->rcp_m = dg::rcp_u32((uint32_t)(dg::kCanvas * G));
-  p->variant = variant;
   p->n_rowtiles = NRT;
   p->rows_per_unit = R;
   p->g = G;
@@ -218,7 +201,6 @@ void make_decode_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
   p->batch = s->batch;
   p->n_q = nq;
   p->rcp_m = dg::rcp_u32((uint32_t)(nq * G));
-  p->variant = dg::kDefaultVariant;  // unused by the decode kernel
   p->n_rowtiles = NRT;
   p->rows_per_unit = R;
   p->g = G;
@@ -391,8 +373,8 @@ dg_status launch(const Call& c, void* stream) {
   }
   if (getenv("DG_LOG")) {
     static const char* const kModeName[] = {"canvas", "commit", "decode"};
-    fprintf(stderr, "[dg] %s dtype=%d variant=%d units=%d R=%d NRT=%d", kModeName[c.mode],
-            dt, c.plan.variant, c.plan.n_units, c.plan.rows_per_unit, c.plan.n_rowtiles);
+    fprintf(stderr, "[dg] %s dtype=%d units=%d R=%d NRT=%d", kModeName[c.mode], dt,
+            c.plan.n_units, c.plan.rows_per_unit, c.plan.n_rowtiles);
     for (int b = 0; b < c.plan.batch; b++)
       fprintf(stderr, " | b%d L=%d S=%d keys/split=%d", b, c.plan.seq[b].prefix_len,
               c.plan.seq[b].n_splits, c.plan.seq[b].split_keys);
@@ -408,9 +390,8 @@ extern "C" {
 size_t dg_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len) {
   if (check_shape(shape) != DG_OK || max_prefix_len < 0 || max_prefix_len > INT32_MAX / 2)
     return 0;
-  // The natural plan never exceeds T + B*Hkv*NRT units whatever the prefixes;
-  // the bound in bytes is largest for the widest row tile.
-  const int R = mfma_path(shape->dtype) ? dg::variant_rows(dg::kVariantR256) : dg::kRowsF32;
+  // The natural plan never exceeds T + B*Hkv*NRT units whatever the prefixes.
+  const int R = rows_per_unit(shape->dtype);
   const int G = shape->n_heads_q / shape->n_heads_kv;
   const int NRT = dg::kCanvas * G / R;
   int64_t units = (int64_t)target_units(shape->dtype) + (int64_t)shape->batch * shape->n_heads_kv * NRT;
@@ -433,7 +414,7 @@ dg_status dg_canvas_attn(const dg_shape* shape, const void* q, const dg_kv* kv_c
 }
 
 dg_status dg_commit_block(const dg_shape* shape, const void* q_blk, const dg_kv* kv_blk,
-                          const dg_kv* kv_cache, const int32_t* prefix_len, void* out,
+                          dg_kv* kv_cache, const int32_t* prefix_len, void* out,
                           void* workspace, size_t ws_bytes, void* stream) {
   Call c;
   dg_status st = prepare(shape, q_blk, kv_cache, prefix_len, kv_blk, out, workspace, ws_bytes,
@@ -460,7 +441,7 @@ size_t dg_decode_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len) 
 }
 
 dg_status dg_decode_attn(const dg_shape* shape, const void* q, const dg_kv* kv_new,
-                         const dg_kv* kv_cache, const int32_t* prefix_len, void* out,
+                         dg_kv* kv_cache, const int32_t* prefix_len, void* out,
                          void* workspace, size_t ws_bytes, void* stream) {
   Call c;
   dg_status st = prepare(shape, q, kv_cache, prefix_len, kv_new, out, workspace, ws_bytes,

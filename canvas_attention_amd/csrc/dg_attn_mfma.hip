@@ -1123,279 +1123,6 @@ __global__ __launch_bounds__(512, 2) void attn_fp8_kernel(AttnArgs a, Plan plan)
 }
 
 // ---------------------------------------------------------------------------
-// Free-running shape: 256 packed rows per unit, NB 32-row blocks per wave (NB = 1:
-// eight waves, two per SIMD; NB = 2: four waves, one per SIMD, whose blocks share
-// every K and V operand read).  No phase barriers: each wave overlaps its own
-// matrix and vector work by software pipelining, issuing the score MFMAs of chunk
-// k+1 between the softmax instructions of chunk k, then the value MFMAs of chunk
-// k and its operand reads for the next chunks; the two waves of a SIMD interleave
-// freely.  One workgroup barrier per chunk serves the ring.
-template <int NB, int MB>
-struct StateN {
-  f32x16 o[NB][MB];  // O^T accumulators of the wave's row blocks
-  float mlog[NB];    // reference maxima (log2 domain)
-  float lsum[NB];    // this lane's share of the row sums
-};
-
-// Chunk max of both row blocks, and the (rare) rescale of either block whose
-// max rose past the threshold; masking first when the chunk needs it.
-template <int NB, int MB, bool CAUSAL>
-__device__ __forceinline__ void prepare_scores_n(f32x16 (&s)[NB], bool masked, int key0, int kstop,
-                                                 int L, const int (&qi)[NB], int h, float c2,
-                                                 StateN<NB, MB>& acc) {
-  if (masked) {
-#pragma unroll
-    for (int rb = 0; rb < NB; rb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int key = key0 + 8 * (i / 4) + 4 * h + (i % 4);
-        bool ok = key < kstop;
-        if (CAUSAL) ok = ok && (key < L || key - L <= qi[rb]);
-        s[rb][i] = ok ? s[rb][i] : -INFINITY;
-      }
-  }
-  float cm[NB];
-  bool rise = false;
-#pragma unroll
-  for (int rb = 0; rb < NB; rb++) {
-    float m = s[rb][0];
-#pragma unroll
-    for (int i = 1; i < 16; i++) m = fmaxf(m, s[rb][i]);
-    cm[rb] = m * c2;
-    rise = rise || cm[rb] > acc.mlog[rb] + kRescaleThreshold;
-  }
-  if (__any(rise)) {
-#pragma unroll
-    for (int rb = 0; rb < NB; rb++) {
-      const float mnew = fmaxf(acc.mlog[rb], partner_max(cm[rb]));
-      const float alpha = __builtin_amdgcn_exp2f(acc.mlog[rb] - mnew);
-      acc.mlog[rb] = mnew;
-      acc.lsum[rb] *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < MB; mb++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc.o[rb][mb][i] *= alpha;
-    }
-  }
-}
-
-template <int D, bool CAUSAL, int NB, int NSLOT>
-__global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(2 / NB, 2 / NB)))
-void attn_rows_kernel(AttnArgs a, Plan plan) {
-  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-  static_assert(NB == 1 || NB == 2, "one or two 32-row blocks per wave");
-  constexpr int NW = 8 / NB, NT = 64 * NW, R = 256;
-  constexpr int KS = D / 16, CH = D / 8, MB = D / 32, ROWB = D * 2, TILEB = 32 * ROWB;
-  constexpr int SSTR = TILEB;                   // one 32-key tile per stage
-  constexpr int GPW = 2 * TILEB / 1024 / NW;    // global_load_lds per wave per stage
-  static_assert(GPW >= 1, "stage load split");
-  static_assert((NSLOT & (NSLOT - 1)) == 0 && NSLOT >= 4, "ring of 4, 8, ... stages");
-  static_assert(NSLOT * SSTR <= kVRegion, "K and V regions of the ring");
-  __shared__ __attribute__((aligned(1024))) char ring[kVRegion + NSLOT * SSTR];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int n = lane & 31, h = lane >> 5;
-  const int U = xcd_remap(blockIdx.x, gridDim.x);
-  SeqPlan sp;
-  const Unit u = decode_unit(plan, U, sp);
-  const int L = sp.prefix_len;
-  const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = plan.g;
-  const int row0 = u.rt * R;
-  int kend = L + kCanvas;
-  if (CAUSAL) kend = min(kend, L + div_rcp(row0 + R - 1, plan.rcp_g) + 1);
-  const int kbeg = u.s * sp.split_keys;
-  const int kstop = min(kbeg + sp.split_keys, kend);
-  const int nstages = kstop > kbeg ? (kstop - kbeg + 31) / 32 : 0;
-
-  const int64_t cap = a.cap;
-  const uint16_t* kc = (const uint16_t*)a.k_cache;
-  const uint16_t* vc = (const uint16_t*)a.v_cache;
-  const uint16_t* kn = (const uint16_t*)a.k_new;
-  const uint16_t* vn = (const uint16_t*)a.v_new;
-
-  // ---- commit: append the block's K/V rows of head g to cache rows L..L+255
-  if (CAUSAL && a.k_append != nullptr) {
-    const int cnt = sp.n_splits * plan.n_rowtiles;
-    const int w = u.s * plan.n_rowtiles + u.rt;
-    const int rpu = (kCanvas + cnt - 1) / cnt;
-    const int r0 = min(kCanvas, w * rpu), r1 = min(kCanvas, r0 + rpu);
-    const int per = (r1 - r0) * CH;
-    for (int idx = tid; idx < 2 * per; idx += NT) {
-      const int which = idx / per, rem = idx % per;
-      const int r = r0 + rem / CH, c = rem % CH;
-      const int64_t src = ((int64_t)(u.b * kCanvas + r) * Hkv + u.g) * D + c * 8;
-      const int64_t dst = (((int64_t)u.b * cap + L + r) * Hkv + u.g) * D + c * 8;
-      const uint4 val = *(const uint4*)((which ? vn : kn) + src);
-      *(uint4*)((uint16_t*)(which ? a.v_append : a.k_append) + dst) = val;
-    }
-  }
-
-  // ---- queries of the wave's row blocks (B operands of S^T = K Q^T)
-  bf16x8 qr[NB][KS];
-  int qi[NB];
-#pragma unroll
-  for (int rb = 0; rb < NB; rb++) {
-    const int prow = row0 + 32 * NB * wave + 32 * rb + n;
-    qi[rb] = div_rcp(prow, plan.rcp_g);
-    const uint16_t* qp = (const uint16_t*)a.q +
-                         ((int64_t)(u.b * kCanvas + qi[rb]) * Hq + u.g * G + prow - qi[rb] * G) * D + (D / 2) * h;
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) qr[rb][ks] = *(const bf16x8*)(qp + 8 * ks);
-  }
-
-  StageLoads<FmtBf16, D, 1, NW> sl;
-  stage_loads_init<FmtBf16, D, 1, NW>(sl, (const char*)(kc + ((int64_t)u.b * cap * Hkv + u.g) * D),
-                             (const char*)(vc + ((int64_t)u.b * cap * Hkv + u.g) * D),
-                             (const char*)(kn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
-                             (const char*)(vn + ((int64_t)u.b * kCanvas * Hkv + u.g) * D),
-                             Hkv * D * 2, L, kstop, wave, lane);
-  const LaneOffsets<D> lo = lane_offsets<D>(lane);
-  const int wave_qi_min = div_rcp(row0 + 32 * NB * wave, plan.rcp_g);
-  const int wave_qi_max = div_rcp(row0 + 32 * NB * wave + 32 * NB - 1, plan.rcp_g);
-  const float c2 = a.scale_log2;
-  // chunks with visible keys for this wave: k < nok; chunks needing masks: k >= kmask
-  const int klimit = CAUSAL ? min(kstop, L + wave_qi_max + 1) : kstop;
-  const int nok = klimit > kbeg ? (klimit - kbeg + 31) / 32 : 0;
-  int kmask = (kstop - kbeg) / 32;
-  if (CAUSAL) {
-    const int x = wave_qi_min + L - 31 - kbeg;
-    kmask = min(kmask, x >= 0 ? x / 32 + 1 : 0);
-  }
-
-  StateN<NB, MB> acc;
-#pragma unroll
-  for (int rb = 0; rb < NB; rb++) {
-#pragma unroll
-    for (int mb = 0; mb < MB; mb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) acc.o[rb][mb][i] = 0.f;
-    acc.mlog[rb] = -1e30f;
-    acc.lsum[rb] = 0.f;
-  }
-
-  const uint32_t lring = lds_addr(ring);
-  uint32_t kaddr[KS], vaddr[MB];
-#pragma unroll
-  for (int ks = 0; ks < KS; ks++) kaddr[ks] = lring + lo.k[ks];
-#pragma unroll
-  for (int mb = 0; mb < MB; mb++) vaddr[mb] = lring + kVRegion + lo.v[mb];
-
-  // ---- ring protocol (barrier B(k) ends chunk k): a wave reads K(j) in chunk j-2
-  //      and V(j) in chunk j-1 and consumes V(j) in chunk j, so stage j is free
-  //      after B(j) and stage j+NSLOT is requested then; K(j) needs stage j
-  //      complete, so before B(j-3) each wave waits for its own loads of it.
-  const int npre = min(NSLOT, nstages);
-  for (int st = 0; st < npre; st++)
-    issue_stage<FmtBf16, D, 1, NW>(lring + (uint32_t)(st & (NSLOT - 1)) * SSTR, kbeg + st * 32, sl);
-  if (nstages >= NSLOT)
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSLOT - 3) * GPW) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-  for (int rb = 0; rb < NB; rb++)
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) asm volatile("" ::"v"(qr[rb][ks]));
-
-  f32x16 sc[NB];       // scores of the chunk whose softmax runs next
-  bf16x8 kop[KS];      // K operands of the next score MFMAs
-  bf16x8 vop[MB][2];   // V^T operands of the next value MFMAs
-  bf16x8 pb[NB][2];    // packed exponentials of the row blocks
-  if (0 < nok) {
-    load_k_operands<D>(kaddr, 0, kop);
-#pragma unroll
-    for (int rb = 0; rb < NB; rb++) scores<D>(kop, qr[rb], sc[rb]);
-    load_v_operands<D>(vaddr, 0, vop);
-  }
-  if (1 < nok) load_k_operands<D>(kaddr, SSTR, kop);
-
-  for (int k0 = 0; k0 < nstages; k0 += NSLOT) {
-#pragma unroll
-    for (int j = 0; j < NSLOT; j++) {
-      const int k = k0 + j;
-      if (k >= nstages) break;
-      const uint32_t off1 = ((j + 1) % NSLOT) * SSTR, off2 = ((j + 2) % NSLOT) * SSTR;
-      f32x16 sn[NB];
-      if (k < nok) {
-        prepare_scores_n<NB, MB, CAUSAL>(sc, k >= kmask, kbeg + 32 * k, kstop, L, qi, h, c2, acc);
-        if (k + 1 < nok) {
-          // scores of chunk k+1 between the exponentials of chunk k
-#pragma unroll
-          for (int rb = 0; rb < NB; rb++) scores<D>(kop, qr[rb], sn[rb]);
-#pragma unroll
-          for (int rb = 0; rb < NB; rb++) numerators(sc[rb], c2, acc.mlog[rb], acc.lsum[rb], pb[rb]);
-#pragma unroll
-          for (int i = 0; i < NB * KS; i++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-          }
-        } else {
-#pragma unroll
-          for (int rb = 0; rb < NB; rb++) numerators(sc[rb], c2, acc.mlog[rb], acc.lsum[rb], pb[rb]);
-        }
-        // K operands of chunk k+2 (read even past the wave's last chunk: unused),
-        // value MFMAs of chunk k, then the V operands of chunk k+1
-        load_k_operands<D>(kaddr, off2, kop);
-#pragma unroll
-        for (int rb = 0; rb < NB; rb++) values<MB>(vop, pb[rb], acc.o[rb]);
-        if (k + 1 < nok) load_v_operands<D>(vaddr, off1, vop);
-      }
-#pragma unroll
-      for (int rb = 0; rb < NB; rb++) sc[rb] = sn[rb];
-      // ---- barrier B(k): stage k+3 complete in every wave's share
-      if (k + NSLOT <= nstages)
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSLOT - 4) * GPW) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      if (k + NSLOT < nstages)
-        issue_stage<FmtBf16, D, 1, NW>(lring + (uint32_t)j * SSTR, kbeg + (k + NSLOT) * 32, sl);
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  // ---- write both row blocks (as the eight-wave kernel does, one block at a time
-  //      through the wave's LDS staging area)
-  const bool direct = sp.n_splits == 1;
-  constexpr int SROWB = 64 * 2 + 16;
-  char* stage = ring + wave * 32 * SROWB;
-  const int r_lo = lane / 8, cq = lane % 8;
-#pragma unroll
-  for (int rb = 0; rb < NB; rb++) {
-    const float lt = partner_sum(acc.lsum[rb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* rowp[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; kk++) {
-      const int p = row0 + 32 * NB * wave + 32 * rb + 8 * kk + r_lo;
-      rowp[kk] = direct ? (uint16_t*)a.out +
-                              ((int64_t)(u.b * kCanvas + div_rcp(p, plan.rcp_g)) * Hq + u.g * G + p - div_rcp(p, plan.rcp_g) * G) * D
-                        : (uint16_t*)a.part_o + ((int64_t)U * R + (p - row0)) * D;
-    }
-#pragma unroll
-    for (int half = 0; half < MB / 2; half++) {
-#pragma unroll
-      for (int mbl = 0; mbl < 2; mbl++)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-          typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4e;
-          bf16x4e v;
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) v[jj] = (__bf16)(acc.o[rb][2 * half + mbl][4 * q4 + jj] * inv);
-          *(bf16x4e*)(stage + n * SROWB + (32 * mbl + 8 * q4 + 4 * h) * 2) = v;
-        }
-#pragma unroll
-      for (int kk = 0; kk < 4; kk++)
-        *(uint4*)(rowp[kk] + 64 * half + 8 * cq) =
-            *(const uint4*)(stage + (8 * kk + r_lo) * SROWB + 16 * cq);
-    }
-    if (!direct && h == 0) {
-      const int prow = row0 + 32 * NB * wave + 32 * rb + n;
-      *(float2*)(a.part_ml + ((int64_t)U * R + (prow - row0)) * 2) = make_float2(acc.mlog[rb], lt);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Decode attention: the AR mode of the same weights and cache, and hybrid
 // decoding that checks several drafted tokens in one pass ("DiffusionGemma
 // Technical Report", paperfeed.app summary, section "The numbers, honestly", the
@@ -1713,19 +1440,6 @@ int launch_one(const AttnArgs& a, const Plan& p, hipStream_t st) {
   return (int)hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int NB, int NSLOT>
-int launch_rows(const AttnArgs& a, const Plan& p, hipStream_t st) {
-  hipLaunchKernelGGL((attn_rows_kernel<D, CAUSAL, NB, NSLOT>), dim3(p.n_units), dim3(512 / NB), 0,
-                     st, a, p);
-  return (int)hipGetLastError();
-}
-
-template <bool CAUSAL>
-int launch_d128(const AttnArgs& a, const Plan& p, hipStream_t st) {
-  if (p.variant == kVariantR256) return launch_one<128, CAUSAL, 8, 1, 8>(a, p, st);
-  if (p.variant == kVariantFree) return launch_rows<128, CAUSAL, 1, 8>(a, p, st);
-  return launch_one<128, CAUSAL, 4, 2, 4>(a, p, st);  // kVariantR128
-}
 
 template <bool CAUSAL>
 int launch_fp8(const AttnArgs& a, const Plan& p, hipStream_t st) {
@@ -1752,8 +1466,9 @@ int launch_decode(const AttnArgs& a, const Plan& p, int dtype, int head_dim, voi
 int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (p.n_units == 0) return 0;
-  if (head_dim == 128) return causal ? launch_d128<true>(a, p, st) : launch_d128<false>(a, p, st);
-  // head_dim 64 has a single shape: 128 rows per unit
+  // 128 packed rows per unit: four row groups x two key groups
+  if (head_dim == 128)
+    return causal ? launch_one<128, true, 4, 2, 4>(a, p, st) : launch_one<128, false, 4, 2, 4>(a, p, st);
   return causal ? launch_one<64, true, 4, 2, 8>(a, p, st) : launch_one<64, false, 4, 2, 8>(a, p, st);
 }
 

@@ -38,19 +38,15 @@ struct SeqPlan {
 // integer division costs tens of dependent instructions before the first load.
 inline uint32_t rcp_u32(uint32_t d) { return d <= 1 ? 0u : (uint32_t)((1ull << 32) / d + 1); }
 
-// bf16 kernel shapes.  R256 and R128: eight waves of 32 packed rows (row groups x
-// key groups, waves paired on a SIMD in ping-pong); Free: eight free-running waves
-// of 32 rows (256 rows per unit).  The fp8 kernel has the R128 shape.
-enum { kVariantR256 = 0, kVariantR128 = 1, kVariantFree = 2, kNumVariants = 3 };
-constexpr int kDefaultVariant = kVariantR128;
-inline int variant_rows(int v) { return v == kVariantR128 ? 128 : 256; }
+// Packed rows per unit of the matrix-core canvas/commit kernels (bf16 and fp8):
+// eight waves of 32 rows, four row groups x two key groups.
+constexpr int kRowsMfma = 128;
 
 struct Plan {
   int32_t batch;
   int32_t n_q;          // query rows per sequence and head: 256 (canvas, commit) or the
                         // decode call's new tokens (1..DG_MAX_DECODE)
   uint32_t rcp_m;       // div_rcp multiplier of n_q * G (packed rows per kv head)
-  int32_t variant;      // bf16 kernel shape (kVariant*); rows_per_unit follows from it
   int32_t n_units;      // total logical units = grid size of the attention kernel (< 2^16)
   int32_t n_rowtiles;   // NRT = ceil(n_q*G / R)
   int32_t rows_per_unit;// R

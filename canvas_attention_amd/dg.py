@@ -146,6 +146,41 @@ def _need(t: torch.Tensor, name: str, dtype, dims: int):
         raise ValueError(f"{name} must be a contiguous {dims}-d tensor")
 
 
+def _check_attn(q, k_cache, v_cache, k_new, v_new, out, names):
+    """Shape agreement of one attention call's tensors.  The C ABI sees only
+    pointers and the sizes in dg_shape / dg_kv, so a cache or K/V tensor with
+    another batch, kv-head count or head_dim than those sizes would be read (and
+    for the commit and decode, written) past its end: reject it here, before any
+    launch.  q and out are [..., B, n, Hq, D]; the caches [B, cap, Hkv, D]; the
+    new K/V [..., B, n, Hkv, D] with q's leading dimensions."""
+    lead, (B, n, Hq, D) = tuple(q.shape[:-4]), tuple(q.shape[-4:])
+    Hkv = k_cache.shape[2]
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"{names[0]} has {Hq} heads, not a multiple of the cache's {Hkv}")
+    if tuple(k_cache.shape) != tuple(v_cache.shape):
+        raise ValueError(f"k_cache {tuple(k_cache.shape)} and v_cache {tuple(v_cache.shape)} differ")
+    if k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError(f"cache {tuple(k_cache.shape)} does not match {names[0]} "
+                         f"{tuple(q.shape)}: expected [{B}, cap, Hkv, {D}]")
+    want = lead + (B, n, Hkv, D)
+    for name, t in ((names[1], k_new), (names[2], v_new)):
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} is {tuple(t.shape)}, expected {want}")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out is {tuple(out.shape)}, expected {tuple(q.shape)}")
+    dev = q.device
+    for t in (k_cache, v_cache, k_new, v_new, out):
+        if t.device != dev:
+            raise ValueError(f"tensors on different devices ({t.device} and {dev})")
+
+
+def _check_workspace(workspace, device):
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device:
+        raise ValueError(f"workspace must be a tensor on {device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -163,11 +198,7 @@ def workspace_bytes(batch, n_heads_q, n_heads_kv, head_dim, max_prefix_len,
                     dtype=torch.bfloat16) -> int:
     """Bytes of workspace any call of this shape needs (see dg_workspace_bytes)."""
     shape = DgShape(_dtype_code(dtype), batch, N_CANVAS, n_heads_q, n_heads_kv, head_dim, 0.0)
-    n = lib.dg_workspace_bytes(ctypes.byref(shape), int(max_prefix_len))
-    if n == 0:
-        # zero is also the answer for a valid shape that needs no partials
-        pass
-    return int(n)
+    return int(lib.dg_workspace_bytes(ctypes.byref(shape), int(max_prefix_len)))
 
 
 def alloc_workspace(q: torch.Tensor, n_heads_kv: int, max_prefix_len: int) -> torch.Tensor:
@@ -190,8 +221,10 @@ def canvas_attn(q, k_cache, v_cache, prefix_len, k_canvas, v_canvas, out=None, w
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype(dt), device=q.device)
     _need(out, "out", out_dtype(dt), 4)
+    _check_attn(q, k_cache, v_cache, k_canvas, v_canvas, out, ("q", "k_canvas", "v_canvas"))
     if workspace is None:
         workspace = alloc_workspace(q, hkv, max(int(x) for x in prefix_len))
+    _check_workspace(workspace, q.device)
     shape = _shape(q, hkv, scale, tensor_scales)
     cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])
     canv = DgKv(k_canvas.data_ptr(), v_canvas.data_ptr(), k_canvas.shape[1])
@@ -215,8 +248,10 @@ def commit_block(q_blk, k_blk, v_blk, k_cache, v_cache, prefix_len, out=None, wo
     if out is None:
         out = torch.empty(q_blk.shape, dtype=out_dtype(dt), device=q_blk.device)
     _need(out, "out", out_dtype(dt), 4)
+    _check_attn(q_blk, k_cache, v_cache, k_blk, v_blk, out, ("q_blk", "k_blk", "v_blk"))
     if workspace is None:
         workspace = alloc_workspace(q_blk, hkv, max(int(x) for x in prefix_len))
+    _check_workspace(workspace, q_blk.device)
     shape = _shape(q_blk, hkv, scale, tensor_scales)
     blk = DgKv(k_blk.data_ptr(), v_blk.data_ptr(), k_blk.shape[1])
     cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])
@@ -250,9 +285,11 @@ def decode_attn(q, k_new, v_new, k_cache, v_cache, prefix_len, out=None, workspa
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype(dt), device=q.device)
     _need(out, "out", out_dtype(dt), 4)
+    _check_attn(q, k_cache, v_cache, k_new, v_new, out, ("q", "k_new", "v_new"))
     if workspace is None:
         n = decode_workspace_bytes(B, k, Hq, hkv, D, max(int(x) for x in prefix_len), dt)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     shape = _shape(q, hkv, scale, tensor_scales)
     new = DgKv(k_new.data_ptr(), v_new.data_ptr(), k_new.shape[1])
     cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])
@@ -276,9 +313,13 @@ def canvas_step_loop(q_steps, k_steps, v_steps, k_cache, v_cache, prefix_len, ou
     if out is None:
         out = torch.empty(q_steps.shape, dtype=out_dtype(dt), device=q_steps.device)
     _need(out, "out", out_dtype(dt), 5)
+    _check_attn(q_steps, k_cache, v_cache, k_steps, v_steps, out, ("q_steps", "k_steps", "v_steps"))
+    if n == 0:
+        return out
     q0 = q_steps[0]
     if workspace is None:
         workspace = alloc_workspace(q0, hkv, max(int(x) for x in prefix_len))
+    _check_workspace(workspace, q0.device)
     shape = _shape(q0, hkv, scale, tensor_scales)
     canv = DgKv(k_steps.data_ptr(), v_steps.data_ptr(), k_steps.shape[2])
     cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])

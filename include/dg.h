@@ -150,7 +150,7 @@ dg_status dg_canvas_attn(const dg_shape* shape, const void* q, const dg_kv* kv_c
  *   workspace  as for dg_canvas_attn
  */
 dg_status dg_commit_block(const dg_shape* shape, const void* q_blk, const dg_kv* kv_blk,
-                          const dg_kv* kv_cache, const int32_t* prefix_len, void* out,
+                          dg_kv* kv_cache, const int32_t* prefix_len, void* out,
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -197,7 +197,7 @@ dg_status dg_canvas_step_loop(const dg_shape* shape, int32_t n_steps, const void
  */
 size_t dg_decode_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len);
 dg_status dg_decode_attn(const dg_shape* shape, const void* q, const dg_kv* kv_new,
-                         const dg_kv* kv_cache, const int32_t* prefix_len, void* out,
+                         dg_kv* kv_cache, const int32_t* prefix_len, void* out,
                          void* workspace, size_t ws_bytes, void* stream);
 
 /*

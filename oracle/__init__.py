@@ -63,6 +63,8 @@ def _load():
         lib.dgo_merge.restype = i32
         lib.dgo_num_threads.argtypes = []
         lib.dgo_num_threads.restype = i32
+        lib.dgo_set_num_threads.argtypes = [i32]
+        lib.dgo_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -112,6 +114,11 @@ def _attn(fn_name, q, k_cache, v_cache, prefix_len, k_new, v_new, scale, rows, t
 def num_threads() -> int:
     """OpenMP threads the oracle's row loops run on."""
     return int(_load().dgo_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of later oracle calls in this process (OpenMP, n >= 1)."""
+    _load().dgo_set_num_threads(int(n))
 
 
 def canvas_attn(q, k_cache, v_cache, prefix_len, k_canvas, v_canvas, scale=None, rows=None,

@@ -204,6 +204,11 @@ static int run(const dgo_args* a, int n_rows, const int32_t* rows, double* out) 
 /* Threads the parallel loops above use (the OpenMP default team size). */
 int dgo_num_threads(void) { return omp_get_max_threads(); }
 
+/* Threads of the following row loops (n >= 1); timing runs use it for a one-thread figure. */
+void dgo_set_num_threads(int n) {
+  if (n >= 1) omp_set_num_threads(n);
+}
+
 /* Canvas step: unmasked attention over [cache rows 0..L-1 ; canvas rows 0..Nc-1].
  * qs, ks, vs: per-tensor scales of the stored q, K and V values. */
 int dgo_canvas_attn(int dtype, int B, int Nc, int Hq, int Hkv, int D, double scale,

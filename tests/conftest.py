@@ -17,3 +17,17 @@ def oracle_lib():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Every parity error the GPU tests measured, against its gate."""
+    try:
+        from helpers import PARITY_RECORDS
+    except ImportError:  # pragma: no cover
+        return
+    if not PARITY_RECORDS:
+        return
+    tr = terminalreporter
+    tr.section("parity: measured error / gate")
+    for test, what, err, gate in PARITY_RECORDS:
+        tr.write_line(f"{err:10.3e} / {gate:8.1e}  {test}  {what}")

@@ -33,6 +33,19 @@ TOL_FP8_RMS = 0.04
 TOL_FP8_ROW = 0.1
 
 
+# Measured parity errors of this session, printed in pytest's terminal summary
+# (tests/conftest.py) so that each gate's margin is on record even under -q.
+PARITY_RECORDS: list = []
+
+
+def record(what: str, err: float, gate: float) -> float:
+    """Log one measured error against its gate (under the current test's name)."""
+    import os
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    PARITY_RECORDS.append((test, what, float(err), float(gate)))
+    return float(err)
+
+
 def to_dev(a: np.ndarray):
     """numpy -> GPU tensor: uint16 holds bf16 bits, uint8 holds e4m3 bytes."""
     import torch

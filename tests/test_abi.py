@@ -262,3 +262,65 @@ def test_selfcond_argument_errors(dg):
     assert f(ctypes.byref(sh), None, FAKE, FAKE, FAKE, FAKE, FAKE, n, None) == -1
     assert f(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, n, None) == -7
     assert f(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n - 1, None) == -5
+
+
+# ---------------------------------------------------------------- binding checks
+# The C ABI sees only pointers and the sizes in dg_shape / dg_kv, so the binding
+# must reject tensors whose shapes disagree before anything is launched: a cache
+# with another batch, kv-head count or head_dim would be read past its end (and
+# written, for the commit and decode).  _check_attn inspects shapes and devices
+# only, so CPU tensors exercise it here.
+
+def _attn_tensors(torch, B=2, n=256, Hq=16, Hkv=8, D=128, cap=300, lead=()):
+    z = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)  # noqa: E731
+    return dict(q=z(*lead, B, n, Hq, D), kc=z(B, cap, Hkv, D), vc=z(B, cap, Hkv, D),
+                kn=z(*lead, B, n, Hkv, D), vn=z(*lead, B, n, Hkv, D), out=z(*lead, B, n, Hq, D))
+
+
+def _check(dg, t, names=("q", "k_canvas", "v_canvas")):
+    dg._check_attn(t["q"], t["kc"], t["vc"], t["kn"], t["vn"], t["out"], names)
+
+
+def test_binding_accepts_matching_shapes(dg):
+    torch = pytest.importorskip("torch")
+    _check(dg, _attn_tensors(torch))
+    _check(dg, _attn_tensors(torch, lead=(3,)), ("q_steps", "k_steps", "v_steps"))
+    _check(dg, _attn_tensors(torch, n=4, Hq=4, Hkv=2, D=64), ("q", "k_new", "v_new"))
+
+
+@pytest.mark.parametrize("keys,shape,msg", [
+    (("kc", "vc"), (1, 300, 8, 128), "does not match"),  # caches of a smaller batch than q's
+    (("kc", "vc"), (2, 300, 8, 64), "does not match"),   # caches of another head_dim
+    (("vc",), (2, 300, 4, 128), "differ"),               # V cache with other kv heads
+    (("kc",), (2, 300, 8, 64), "differ"),                # K cache with another head_dim
+    (("kn",), (2, 256, 4, 128), "expected"),             # canvas K with other kv heads
+    (("vn",), (1, 256, 8, 128), "expected"),             # canvas V with another batch
+    (("kn",), (2, 128, 8, 128), "expected"),             # canvas K with fewer rows
+    (("out",), (2, 256, 16, 64), "expected"),            # output of another shape
+])
+def test_binding_rejects_mismatched_shapes(dg, keys, shape, msg):
+    torch = pytest.importorskip("torch")
+    t = _attn_tensors(torch)
+    for key in keys:
+        t[key] = torch.zeros(*shape, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=msg):
+        _check(dg, t)
+
+
+def test_binding_rejects_head_counts_that_do_not_divide(dg):
+    torch = pytest.importorskip("torch")
+    t = _attn_tensors(torch, Hkv=6)
+    with pytest.raises(ValueError, match="multiple"):
+        _check(dg, t)
+
+
+def test_binding_step_tensors_hold_n_steps(dg):
+    torch = pytest.importorskip("torch")
+    t = _attn_tensors(torch, lead=(12,))
+    t["kn"] = torch.zeros(11, 2, 256, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="expected"):
+        _check(dg, t, ("q_steps", "k_steps", "v_steps"))
+    t = _attn_tensors(torch, lead=(12,))
+    t["out"] = torch.zeros(11, 2, 256, 16, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="expected"):
+        _check(dg, t, ("q_steps", "k_steps", "v_steps"))

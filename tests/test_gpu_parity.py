@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from canvas_attention_amd import synth
-from helpers import TOL_BF16, TOL_F32, row_err, sample_rows, to_dev, to_host_bits, to_host_f64
+from helpers import TOL_BF16, TOL_F32, record, row_err, to_dev, to_host_bits, to_host_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -52,18 +52,26 @@ def run_canvas(c, ws=None):
     return out
 
 
-def check_canvas(c, tol, rows=None):
+def check_canvas(c, tol, what="canvas step"):
+    """Every output row of one canvas step against the oracle."""
     out = to_host_f64(run_canvas(c))
-    ref = oracle_canvas(c, rows)
-    got = out if rows is None else out[rows[:, 0], rows[:, 1], rows[:, 2]]
-    err = row_err(got, ref)
+    err = record(what, row_err(out, oracle_canvas(c)), tol)
     assert err <= tol, f"per-row error {err:.3e} > {tol}"
     return err
 
 
-def oracle_canvas(c, rows=None):
+def oracle_canvas(c):
     import oracle
-    return oracle.canvas_attn(c["q"], c["kc"], c["vc"], c["L"], c["kn"], c["vn"], rows=rows)
+    return oracle.canvas_attn(c["q"], c["kc"], c["vc"], c["L"], c["kn"], c["vn"])
+
+
+def check_commit(oracle_lib, qb, kb, vb, kc, vc, L, out, what="commit"):
+    """Every output row of one commit against the oracle (kc, vc: the cache
+    before the append)."""
+    ref = oracle_lib.commit_attn(qb, kc, vc, L, kb, vb)
+    err = record(what, row_err(to_host_f64(out), ref), TOL_BF16)
+    assert err <= TOL_BF16, f"{what}: per-row error {err:.3e} > {TOL_BF16}"
+    return err
 
 
 # --------------------------------------------------------------- fp32 workload
@@ -78,14 +86,13 @@ def test_tiny_fp32_step_and_commit(oracle_lib, split_keys, forced):
     seed, Hq, Hkv, D = w["seed"], w["hq"], w["hkv"], w["d"]
     cap = 320
     c = make(seed, 1, L, Hq, Hkv, D, "f32", cap=cap)
-    err = check_canvas(c, TOL_F32)
-    print(f"fp32 step err {err:.2e}")
+    check_canvas(c, TOL_F32, f"fp32 canvas step, split {forced}")
     qb, kb, vb = synth.block(seed, 1, Hq, Hkv, D, "f32")
     kc_d, vc_d = to_dev(c["kc"]), to_dev(c["vc"])
     out = dg.commit_block(to_dev(qb), to_dev(kb), to_dev(vb), kc_d, vc_d, L)
     torch.cuda.synchronize()
     ref = oracle_lib.commit_attn(qb, c["kc"], c["vc"], L, kb, vb)
-    err = row_err(to_host_f64(out), ref)
+    err = record(f"fp32 commit, split {forced}", row_err(to_host_f64(out), ref), TOL_F32)
     assert err <= TOL_F32, err
     kc2, vc2 = c["kc"].copy(), c["vc"].copy()
     oracle_lib.append_block(kb, vb, kc2, vc2, L)
@@ -100,8 +107,7 @@ def test_step_l2k_full(oracle_lib):
     w = synth.WORKLOADS["step_l2k"]
     c = make(w["seed"], 1, synth.prefix_lengths("step_l2k"), w["hq"], w["hkv"], w["d"], "bf16",
              cap=2048)
-    err = check_canvas(c, TOL_BF16)
-    print(f"L=2048 err {err:.2e}")
+    check_canvas(c, TOL_BF16, "L=2048 canvas step")
 
 
 @pytest.mark.parametrize("B,L,Hq,Hkv,D,forced", [
@@ -116,8 +122,7 @@ def test_step_l2k_full(oracle_lib):
 def test_canvas_small_shapes(oracle_lib, split_keys, B, L, Hq, Hkv, D, forced):
     split_keys(forced)
     c = make(7, B, L, Hq, Hkv, D, "bf16")
-    err = check_canvas(c, TOL_BF16)
-    print(f"B={B} L={L} G={Hq // Hkv} D={D} split={forced}: err {err:.2e}")
+    check_canvas(c, TOL_BF16, f"B={B} L={L} G={Hq // Hkv} D={D} split={forced}")
 
 
 @pytest.mark.parametrize("forced", [128, 160, 192, 256, 288, 352, 416])
@@ -128,8 +133,7 @@ def test_canvas_ring_depths(oracle_lib, split_keys, forced, L):
     of the ring protocol take their counted and their full waits."""
     split_keys(forced)
     c = make(31, 1, [L], 16, 8, 128, "bf16")
-    err = check_canvas(c, TOL_BF16)
-    print(f"L={L} split={forced}: err {err:.2e}")
+    check_canvas(c, TOL_BF16, f"L={L} split={forced}")
 
 
 @pytest.mark.parametrize("forced", [128, 192, 288, 416])
@@ -144,20 +148,15 @@ def test_commit_ring_depths(oracle_lib, split_keys, forced):
     kc_d, vc_d = to_dev(kc), to_dev(vc)
     out = dg.commit_block(to_dev(qb), to_dev(kb), to_dev(vb), kc_d, vc_d, Ls)
     torch.cuda.synchronize()
-    ref = oracle_lib.commit_attn(qb, kc, vc, Ls, kb, vb)
-    err = row_err(to_host_f64(out), ref)
-    assert err <= TOL_BF16, err
-    print(f"commit split={forced}: err {err:.2e}")
+    check_commit(oracle_lib, qb, kb, vb, kc, vc, Ls, out, f"commit split={forced}")
 
 
-def test_canvas_long_context_sampled(oracle_lib):
-    """bf16 L=131072: split-key merge and cache streaming; sampled rows."""
+def test_canvas_long_context_full(oracle_lib):
+    """bf16 L=131072: split-key merge and cache streaming; every output row."""
     w = synth.WORKLOADS["long_l128k"]
     L = synth.prefix_lengths("long_l128k")
     c = make(w["seed"], 1, L, w["hq"], w["hkv"], w["d"], "bf16", cap=int(L[0]))
-    rows = sample_rows(np.random.default_rng(0), 1, 256, 16, 48)
-    err = check_canvas(c, TOL_BF16, rows)
-    print(f"L=131072 sampled err {err:.2e}")
+    check_canvas(c, TOL_BF16, "L=131072 canvas step")
 
 
 def test_rising_scores_exercise_rescale(oracle_lib, split_keys):
@@ -169,8 +168,7 @@ def test_rising_scores_exercise_rescale(oracle_lib, split_keys):
     c["kc"] = synth.bf16_round(f * ramp)
     q = synth.bf16_to_f32(c["q"]) * 2.0
     c["q"] = synth.bf16_round(q)
-    err = check_canvas(c, TOL_BF16)
-    print(f"rising scores err {err:.2e}")
+    check_canvas(c, TOL_BF16, "rising scores")
 
 
 def test_determinism(split_keys):
@@ -198,18 +196,16 @@ def test_commit_small(oracle_lib, split_keys, B, L, Hq, Hkv, D, forced):
     kc_d, vc_d = to_dev(kc), to_dev(vc)
     out = dg.commit_block(to_dev(qb), to_dev(kb), to_dev(vb), kc_d, vc_d, Ls)
     torch.cuda.synchronize()
-    ref = oracle_lib.commit_attn(qb, kc, vc, Ls, kb, vb)
-    err = row_err(to_host_f64(out), ref)
-    assert err <= TOL_BF16, err
+    check_commit(oracle_lib, qb, kb, vb, kc, vc, Ls, out, f"commit B={B} L={L} split={forced}")
     oracle_lib.append_block(kb, vb, kc, vc, Ls)
     np.testing.assert_array_equal(to_host_bits(kc_d), kc)
     np.testing.assert_array_equal(to_host_bits(vc_d), vc)
-    print(f"commit B={B} L={L} err {err:.2e}")
 
 
 def test_block_cycle_l8k(oracle_lib):
     """12 canvas steps against a fixed L=8192 cache (loop == single calls, bit for
-    bit), then the commit (L -> 8448), then a step on the grown cache."""
+    bit), then the commit (L -> 8448), then a step on the grown cache; every
+    output row of all 14 calls against the oracle."""
     w = synth.WORKLOADS["cycle_l8k"]
     seed, Hq, Hkv, D = w["seed"], w["hq"], w["hkv"], w["d"]
     L = synth.prefix_lengths("cycle_l8k")
@@ -225,35 +221,31 @@ def test_block_cycle_l8k(oracle_lib):
     torch.cuda.synchronize()
     for s in range(12):
         assert torch.equal(loop_out[s], singles[s]), f"step {s}: loop differs from single call"
-    rng = np.random.default_rng(1)
-    for s in (0, 11):
-        rows = sample_rows(rng, 1, 256, Hq, 96)
-        ref = oracle_lib.canvas_attn(steps[s][0], kc, vc, L, steps[s][1], steps[s][2], rows=rows)
-        got = to_host_f64(loop_out[s])[rows[:, 0], rows[:, 1], rows[:, 2]]
-        assert row_err(got, ref) <= TOL_BF16
+    for s in range(12):
+        ref = oracle_lib.canvas_attn(steps[s][0], kc, vc, L, steps[s][1], steps[s][2])
+        err = record(f"L=8192 step {s}", row_err(to_host_f64(loop_out[s]), ref), TOL_BF16)
+        assert err <= TOL_BF16, f"step {s}: {err:.3e}"
     qb, kb, vb = synth.block(seed, 1, Hq, Hkv, D, "bf16")
     out = dg.commit_block(to_dev(qb), to_dev(kb), to_dev(vb), kc_d, vc_d, L)
     torch.cuda.synchronize()
-    rows = sample_rows(rng, 1, 256, Hq, 128)
-    ref = oracle_lib.commit_attn(qb, kc, vc, L, kb, vb, rows=rows)
-    got = to_host_f64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
-    err_c = row_err(got, ref)
-    assert err_c <= TOL_BF16
+    check_commit(oracle_lib, qb, kb, vb, kc, vc, L, out, "L=8192 commit")
     oracle_lib.append_block(kb, vb, kc, vc, L)
     np.testing.assert_array_equal(to_host_bits(kc_d), kc)
+    np.testing.assert_array_equal(to_host_bits(vc_d), vc)
     L2 = L + 256
     q2, k2, v2 = synth.canvas(seed, 1, Hq, Hkv, D, "bf16", block=1)
     out2 = dg.canvas_attn(to_dev(q2), kc_d, vc_d, L2, to_dev(k2), to_dev(v2))
     torch.cuda.synchronize()
-    ref2 = oracle_lib.canvas_attn(q2, kc, vc, L2, k2, v2, rows=rows)
-    got2 = to_host_f64(out2)[rows[:, 0], rows[:, 1], rows[:, 2]]
-    assert row_err(got2, ref2) <= TOL_BF16
-    print(f"cycle ok, commit err {err_c:.2e}")
+    ref2 = oracle_lib.canvas_attn(q2, kc, vc, L2, k2, v2)
+    err = record("L=8448 step after the commit", row_err(to_host_f64(out2), ref2), TOL_BF16)
+    assert err <= TOL_BF16
 
 
 def test_ragged_multi_block_generation(oracle_lib):
     """Batch of 8 sequences with seeded prefixes in [1024, 32768]; 4 blocks of
-    (12 steps + commit); sampled rows of selected steps and of every commit."""
+    (12 steps + commit).  Every output row of one seeded step per block and of
+    every commit against the oracle; every step of the loop equals its single
+    call bit for bit; the cache ends equal to the oracle's appends."""
     w = synth.WORKLOADS["ragged_b8"]
     seed, B, Hq, Hkv, D = w["seed"], w["batch"], w["hq"], w["hkv"], w["d"]
     L = synth.prefix_lengths("ragged_b8").copy()
@@ -269,18 +261,17 @@ def test_ragged_multi_block_generation(oracle_lib):
         ks = torch.stack([to_dev(s[1]) for s in steps])
         vs = torch.stack([to_dev(s[2]) for s in steps])
         out = dg.canvas_step_loop(qs, ks, vs, kc_d, vc_d, L, workspace=ws)
-        torch.cuda.synchronize()
         s = int(rng.integers(12))
-        rows = sample_rows(rng, B, 256, Hq, 64)
-        ref = oracle_lib.canvas_attn(steps[s][0], kc, vc, L, steps[s][1], steps[s][2], rows=rows)
-        got = to_host_f64(out[s])[rows[:, 0], rows[:, 1], rows[:, 2]]
-        assert row_err(got, ref) <= TOL_BF16, f"block {blk} step {s}"
+        single = dg.canvas_attn(qs[s], kc_d, vc_d, L, ks[s], vs[s], workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out[s], single), f"block {blk} step {s}: loop differs from single call"
+        ref = oracle_lib.canvas_attn(steps[s][0], kc, vc, L, steps[s][1], steps[s][2])
+        err = record(f"ragged block {blk} step {s}", row_err(to_host_f64(out[s]), ref), TOL_BF16)
+        assert err <= TOL_BF16, f"block {blk} step {s}: {err:.3e}"
         qb, kb, vb = synth.block(seed, B, Hq, Hkv, D, "bf16", block=blk)
         outc = dg.commit_block(to_dev(qb), to_dev(kb), to_dev(vb), kc_d, vc_d, L, workspace=ws)
         torch.cuda.synchronize()
-        refc = oracle_lib.commit_attn(qb, kc, vc, L, kb, vb, rows=rows)
-        gotc = to_host_f64(outc)[rows[:, 0], rows[:, 1], rows[:, 2]]
-        assert row_err(gotc, refc) <= TOL_BF16, f"block {blk} commit"
+        check_commit(oracle_lib, qb, kb, vb, kc, vc, L, outc, f"ragged block {blk} commit")
         oracle_lib.append_block(kb, vb, kc, vc, L)
         L = L + 256
     np.testing.assert_array_equal(to_host_bits(kc_d), kc)

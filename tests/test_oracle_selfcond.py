@@ -57,6 +57,16 @@ def test_gelu_tanh_against_the_erf_form():
     np.testing.assert_allclose(selfcond.gelu_tanh(big), [30.0, 0.0], atol=1e-12)
 
 
+def test_gelu_tanh_against_torch_tanh_gelu():
+    """The tanh form against torch's own tanh-approximated GELU in float64 on the
+    CPU: an independent implementation of the same formula, so a wrong constant
+    (a digit swap in 0.044715 moves values by about 1e-5) fails at 1e-14."""
+    torch = pytest.importorskip("torch")
+    x = np.linspace(-8, 8, 4001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    np.testing.assert_allclose(selfcond.gelu_tanh(x), ref, rtol=0, atol=1e-14)
+
+
 def test_brute_force_tiny():
     """Every step written out with Python loops and math.exp / math.tanh."""
     M, V, d, h = 3, 7, 4, 5
