@@ -359,6 +359,44 @@ __device__ __forceinline__ void issue_stage(uint32_t slot, int skey0, const Stag
   }
 }
 
+// The scalar half of a stage request, formed one phase ahead of the loads: where
+// the stage's keys come from (stage_source) and, for a stage wholly in the cache
+// or wholly in the canvas, its scalar base address.  issue_stage_req then costs
+// the matrix phase only an m0 write and the loads themselves.
+struct StageReq {
+  int src;
+  uint64_t base;
+};
+
+template <class F, int D, int WK, int NW>
+__device__ __forceinline__ StageReq stage_req(int skey0, const StageLoads<F, D, WK, NW>& sl) {
+  StageReq r;
+  r.src = stage_source(skey0, sl);
+  r.base = (r.src == 1 ? sl.cb : sl.nb) + (uint64_t)(int64_t)skey0 * (uint64_t)sl.rsb + sl.rowoff;
+  return r;
+}
+
+template <class F, int D, int WK, int NW>
+__device__ __forceinline__ void issue_stage_req(uint32_t slot, int skey0, const StageReq& r,
+                                                const StageLoads<F, D, WK, NW>& sl) {
+  using SL = StageLoads<F, D, WK, NW>;
+  constexpr int G = SL::GPW;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + sl.dst);
+  if (r.src > 0) {
+    gll_block<G>(uniform_ptr((const char*)(uintptr_t)r.base), sl.lane, m0);
+  } else {
+#pragma unroll
+    for (int e = 0; e < G; e++) {
+      const int key = min(skey0 + sl.krow + e * SL::RPI, sl.kstop - 1);
+      const uint64_t base = key < sl.L ? sl.cb : sl.nb;
+      const uint64_t row = base + (uint64_t)(int64_t)key * (uint64_t)sl.rsb;
+      const uint32_t chunk = sl.lane[e] + 1024u * (uint32_t)e -
+                             (uint32_t)(sl.krow - (sl.krow / SL::RPI) * SL::RPI + e * SL::RPI) * (uint32_t)sl.rsb;
+      gll_vaddr((const char*)(uintptr_t)(row + chunk), m0 + 1024u * (uint32_t)e);
+    }
+  }
+}
+
 // V^T operands of one 32-key chunk: vop[mb][t] holds, in lane (d, h), the values
 // of keys 16t + 8r + 4h + e (k-slot 4r + e) at head_dim 32mb + d, read with the
 // transposing ds_read_b64_tr_b16.  vbase[mb] is the lane's address in stage 0;
@@ -536,6 +574,31 @@ template <int MB, int D>
 __device__ __forceinline__ void values(const Ops16<D>& op, State<MB>& acc) {
   values<MB>(op.v, op.p, acc);
 }
+
+// Slices of the matrix phase, so that loads and LDS reads can be placed between
+// single MFMAs.  Value MFMA i (0 .. 2*MB-1) adds head_dim block i % MB of keys
+// 16*(i / MB) .. +15: the first MB are independent of each other.
+template <int D>
+constexpr int n_value_mfma(const Ops16<D>*) { return D / 16; }
+template <int MB, int D>
+__device__ __forceinline__ void value_mfma(int i, const Ops16<D>& op, State<MB>& acc) {
+  const int mb = i % MB, t = i / MB;
+  acc.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.v[mb][t], op.p[t], acc.o[mb], 0, 0, 0);
+}
+// Score MFMA ks of the next chunk, then the K operand ks of the chunk after it read
+// into the registers the MFMA has just taken (koff: that chunk's stage offset).
+template <int D>
+__device__ __forceinline__ void score_mfma_and_k(int ks, Ops16<D>& op, const uint32_t (&kbase)[D / 16],
+                                                 uint32_t koff, bool read_k) {
+  if (ks == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) op.s[0][i] = 0.f;
+  }
+  op.s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.k[ks], op.q[ks], op.s[0], 0, 0, 0);
+  if (read_k) op.k[ks] = *(const LDS_AS bf16x8*)(uintptr_t)(kbase[ks] + koff);
+}
+template <int D>
+constexpr int n_score_mfma(const Ops16<D>*) { return D / 16; }
 
 // ---------------------------------------------------------------------------
 // fp8 operands.  v_mfma_f32_32x32x64_f8f6f4 multiplies byte j of A lane (i, h)
@@ -722,26 +785,47 @@ __device__ __forceinline__ void values(Ops8& op, State<MB>& acc) {
   op.rs = mfma_f8(op.ones, op.p, op.rs);
 }
 
+// fp8 slices: value MFMAs 0 .. MB-1 take head_dim blocks, MFMA MB the row sums;
+// score MFMA i = 2t + ks covers key half t, head_dim half ks.
+constexpr int n_value_mfma(const Ops8*) { return 5; }
+template <int MB>
+__device__ __forceinline__ void value_mfma(int i, Ops8& op, State<MB>& acc) {
+  if (i < MB) acc.o[i] = mfma_f8(op.v[i], op.p, acc.o[i]);
+  else op.rs = mfma_f8(op.ones, op.p, op.rs);
+}
+__device__ __forceinline__ void score_mfma_and_k(int i, Ops8& op, const uint32_t (&kbase)[2][2],
+                                                 uint32_t koff, bool read_k) {
+  const int t = i >> 1, ks = i & 1;
+  if (ks == 0) {
+#pragma unroll
+    for (int e = 0; e < 16; e++) op.s[t][e] = 0.f;
+  }
+  op.s[t] = mfma_f8(op.k[t][ks], op.q[ks], op.s[t]);
+  if (read_k)
+    op.k[t][ks] = lds_read_2x16(kbase[ks][0] + koff + 4096u * t, kbase[ks][1] + koff + 4096u * t);
+}
+constexpr int n_score_mfma(const Ops8*) { return 4; }
+
 // The kernel.  Wave (rg, kg) processes chunk k = tile k*WK + kg of the unit for
 // k = 0 .. nstages-1; chunk k lives in ring stage k (slot k mod NSLOT).  Per chunk
 // a wave runs
-//   X(k): requests stage k+NSLOT, O += V(k) P(k) (bf16: 8 MFMAs, fp8: 4),
-//         S(k+1) = K(k+1) Q^T (bf16: 8 MFMAs, fp8: 4) with the V(k+1) operand
-//         reads between them
-//   Y(k): K(k+2) operand reads, softmax of S(k+1) -> P(k+1)
+//   X(k): O += V(k) P(k) (bf16: 8 MFMAs, fp8: 4 and the row-sum MFMA) with the
+//         loads of stage k+NSLOT issued behind the first of them, then
+//         S(k+1) = K(k+1) Q^T (bf16: 8 MFMAs, fp8: 4) with the reads of the V(k+1)
+//         and K(k+2) operands placed between them;
+//   Y(k): softmax of S(k+1) -> P(k+1) (vector ALU only).
 // One workgroup barrier per chunk: barrier k follows Y(k) in waves 0-3 (group 0)
 // and X(k) in waves 4-7 (group 1), so group 1 runs half a chunk behind and, on
 // each SIMD, one wave is in X while the other is in Y.  Between barriers k-1 and
 // k group 0 runs X(k), Y(k) and group 1 runs Y(k-1), X(k).
 // Ring protocol: every barrier first waits for the wave's LDS reads.  The reads
-// of stage k (V(k) in X(k-1), K(k) in Y(k-2), which for group 1 falls between
-// barriers k-2 and k-1) are then done at barrier k-1, after which X(k) may
-// request stage k+NSLOT into the same slot.  The first read of stage s is group
-// 0's K(s) in Y(s-2), after barrier s-3; so before barrier k every wave waits for
-// its own loads of stage k+3, leaving stages k+4 .. k+NSLOT in flight.  Stage 2
-// is requested only after the prologue (its slot holds the queries until then),
-// yet group 0 reads K(2) in Y(0); one extra barrier E, after group 0's X(0) and
-// before group 1's X(0), waits for it.
+// of stage s are K(s) in X(s-2) and V(s) in X(s-1), both groups, between barriers
+// s-3 and s-1; so all reads of stage k are done at barrier k-1, after which X(k)
+// may request stage k+NSLOT into the same slot, and before barrier k every wave
+// waits for its own loads of stage k+3, leaving stages k+4 .. k+NSLOT in flight.
+// The prologue requests stages 0 .. NSLOT-1 together with the queries (which
+// have their own LDS area); barrier A (queries and stage 0 in) precedes the first
+// scores and barrier B (stages 1 and 2 in) the first K(2) reads.
 // One body serves both formats (F = FmtBf16 or FmtFp8); the entry points are
 // attn_bf16_kernel and attn_fp8_kernel below.
 template <class F, int D, bool CAUSAL, int WM, int WK, int NSLOT>
@@ -769,7 +853,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const Plan& plan) {
   // score MFMAs per chunk and the V operand reads issued between them
   constexpr int NSM = F8 ? 4 : KS, NVR = 4 * MB;
   static_assert(NVR % NSM == 0, "V reads spread evenly over the score MFMAs");
-  __shared__ __attribute__((aligned(1024))) char ring[NSLOT * SLOTB];
+  constexpr int QBYTES = R * ROWB;      // the unit's query rows, past the ring
+  static_assert(NSLOT * SLOTB + QBYTES <= 163840, "ring and queries fit a CU's LDS");
+  __shared__ __attribute__((aligned(1024))) char ring[NSLOT * SLOTB + QBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -821,31 +907,23 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const Plan& plan) {
                                 kn + ((int64_t)u.b * kCanvas * Hkv + u.g) * ROWB,
                                 vn + ((int64_t)u.b * kCanvas * Hkv + u.g) * ROWB,
                                 Hkv * ROWB, L, kstop, wave, lane);
-  // The first two stages (the operands of the first chunk and the scores of the
-  // second) are requested as soon as the unit is known; everything below overlaps
-  // their flight.  Only these two precede the first wait: the compiler's wait for
-  // the query registers also covers every load issued before it.
   static_assert((NSLOT & (NSLOT - 1)) == 0, "ring of a power-of-two number of stages");
   constexpr uint32_t SSTR = WK * TILEB;  // stage stride within the K (or V) region
   static_assert(NSLOT * SSTR <= kVRegion, "K and V regions of the ring");
   const uint32_t lring = lds_addr(ring);
   auto stage_slot = [&](int slot) { return lring + (uint32_t)slot * SSTR; };
-  // The unit's R query rows travel the same way, into ring space that stages 2..
-  // take over only when the prologue ends: rows 0..QRH-1 at offset 32 KB of the K
-  // region, the rest at the same offset of the V region, swizzled like a K tile
-  // (bf16: chunk ^ row % CH; fp8: chunk ^ swz8(row)), so that each wave reads its
-  // B operands with conflict-free 16-byte reads.  Loaded per lane straight into
-  // registers, every instruction would touch 64 cache lines (32 rows, 16 bytes of
-  // each), and both key groups would fetch the same rows.
-  constexpr int QRH = 32768 / ROWB;       // query rows per 32 KB half
+  // The unit's R query rows travel by the same DMA into their own LDS area past
+  // the ring, swizzled like a K tile (bf16: chunk ^ row % CH; fp8: chunk ^
+  // swz8(row)), so that each wave reads its B operands with conflict-free 16-byte
+  // reads.  Loaded per lane straight into registers, every instruction would touch
+  // 64 cache lines (32 rows, 16 bytes of each), and both key groups would fetch
+  // the same rows.  With the queries out of the ring, every stage of the ring is
+  // requested as soon as the unit is known.
   constexpr int QRW = R / 8;              // rows loaded per wave
   constexpr int QPW = QRW * ROWB / 1024;  // loads per wave
   constexpr int QRPI = 1024 / ROWB;       // rows per load
-  static_assert(2 * SSTR <= 32768 && R <= 2 * QRH && QRH % QRW == 0 && QPW >= 1,
-                "queries fit the ring space of stages 2..");
-  auto q_lds = [&](int r) {
-    return lring + (uint32_t)(r / QRH) * kVRegion + 32768u + (uint32_t)(r % QRH) * ROWB;
-  };
+  static_assert(QPW >= 1 && QRW % QRPI == 0, "whole 1 KB query loads per wave");
+  auto q_lds = [&](int r) { return lring + (uint32_t)(NSLOT * SLOTB) + (uint32_t)r * ROWB; };
   {
     const char* qb = uniform_ptr((const char*)a.q + ((int64_t)u.b * kCanvas * Hq + u.g * G) * ROWB);
     const int r_first = wave * QRW;
@@ -863,7 +941,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const Plan& plan) {
       gll_block<NB4>(qb, vo, __builtin_amdgcn_readfirstlane(q_lds(r_first + j * QRPI)));
     }
   }
-  const int npre = min(2, nstages);
+  const int npre = min(NSLOT, nstages);
   for (int st = 0; st < npre; st++) issue_stage<F, D, WK, 8>(stage_slot(st), kbeg + st * WK * TK, sl);
 
   const auto lo = [&] {
@@ -900,6 +978,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const Plan& plan) {
   const int kmask = tmask > kg ? (tmask - kg + WK - 1) / WK : 0;
 
   auto chunk_key = [&](int k) { return kbeg + (k * WK + kg) * TK; };
+  auto stage_key = [&](int st) { return kbeg + st * WK * TK; };
   // per-lane operand addresses in stage 0 of this wave's key group
   using Ops = typename std::conditional<F8, Ops8, Ops16<D>>::type;
   using KAddr = typename std::conditional<F8, uint32_t[2][2], uint32_t[KS]>::type;
@@ -924,11 +1003,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const Plan& plan) {
     for (int mb = 0; mb < MB; mb++) vaddr[mb] = lring + kVRegion + kg * TILEB + lo.v[mb];
   }
 
-  // ---- prologue.  Barrier A: the queries and stage 0 (the wave's own loads of
-  //      them are its oldest npre*GPW .. ones) are in LDS; the wave reads its query
-  //      operands and starts on chunk 0.  Barrier B: stage 1 is in, and every wave
-  //      has read its queries, so the rest of the ring may overwrite them.
-  if (npre == 2)
+  // ---- prologue.  Barrier A: the queries and stage 0 (the wave's oldest loads)
+  //      are in LDS; the wave reads its query operands and the scores of chunk 0.
+  //      Barrier B: stages 1 and 2 are in (the chunk loop reads K(2) in its first
+  //      matrix phase); stages 3.. may still be in flight.
+  // (vmcnt counts a wave's loads in issue order: queries, then stages 0, 1, ...)
+  if (npre == NSLOT)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSLOT - 1) * GPW) : "memory");
+  else if (npre == 3)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * GPW) : "memory");
+  else if (npre == 2)
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(GPW) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -946,31 +1030,28 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const Plan& plan) {
     scores(op);
     load_v_operands(vaddr, 0, op);
   }
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int st = 2; st < min(NSLOT, nstages); st++)
-    issue_stage<F, D, WK, 8>(stage_slot(st), kbeg + st * WK * TK, sl);
+  if (npre == NSLOT)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NSLOT - 3) * GPW) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (1 < nok) load_k_operands(kaddr, SSTR % (NSLOT * SSTR), op);
   if (0 < nok) {
     prepare_scores<MB, CAUSAL>(op, 0 >= kmask, chunk_key(0), kstop, L, qi, h, c2, acc);
     numerators<MB>(op, c2, acc);
   }
+  // the scalar half of X(0)'s stage request
+  StageReq req = stage_req(stage_key(NSLOT), sl);
 
-  auto barrier_e = [&](bool after_x0) {  // barrier E: stage 2 complete
-    if (NSLOT < nstages) {
-      if (after_x0)  // stages 3 .. NSLOT may be in flight
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NSLOT - 2) * GPW) : "memory");
-      else           // stages 3 .. NSLOT-1 may be in flight
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NSLOT - 3) * GPW) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-  };
   auto ring_barrier = [&](int k) {  // barrier k (see the kernel comment)
     if (k + NSLOT < nstages)
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NSLOT - 3) * GPW) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
+  constexpr int NVM = n_value_mfma((const Ops*)nullptr);  // value (and row-sum) MFMAs per chunk
+  constexpr int NSC = n_score_mfma((const Ops*)nullptr);  // score MFMAs per chunk
+  constexpr int NRD = (NVR + (F8 ? 8 : KS)) / NSC;         // LDS reads placed after each score MFMA
+  static_assert((NVR + (F8 ? 8 : KS)) % NSC == 0, "LDS reads spread evenly over the score MFMAs");
 
   // The chunk loop is unrolled over the ring so that every stage offset is a
   // compile-time immediate of the LDS instructions.
@@ -980,35 +1061,43 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const Plan& plan) {
       const int k = k0 + j;
       if (k >= nstages) break;
       const uint32_t off1 = ((j + 1) % NSLOT) * SSTR, off2 = ((j + 2) % NSLOT) * SSTR;
-      // X(k): loads of stage k+NSLOT (into the slot of stage k); the value
-      // product of chunk k; the V operands of chunk k+1 read while the scores of
-      // chunk k+1 run (the issue slots of an MFMA phase are otherwise idle)
+      // X(k), the matrix phase: the value product of chunk k with the loads of
+      // stage k+NSLOT (into the slot of stage k) behind its first MFMA, then the
+      // scores of chunk k+1 with the reads of the V operands of chunk k+1 and of
+      // the K operands of chunk k+2 (a chunk past the wave's last is read too and
+      // not used) placed between them: the issue slots of an MFMA phase are
+      // otherwise idle, and the vector phase keeps only the softmax.
       __builtin_amdgcn_sched_barrier(0);
-      if (grp == 1 && k == 0) barrier_e(false);
-      if (k + NSLOT < nstages) issue_stage<F, D, WK, 8>(stage_slot(j), kbeg + (k + NSLOT) * WK * TK, sl);
       __builtin_amdgcn_s_setprio(1);
-      if (k < nok) values<MB>(op, acc);
+      if (k < nok) value_mfma<MB>(0, op, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + NSLOT < nstages) issue_stage_req(stage_slot(j), stage_key(k + NSLOT), req, sl);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k < nok) {
+#pragma unroll
+        for (int i = 1; i < NVM; i++) value_mfma<MB>(i, op, acc);
+      }
       if (k + 1 < nok) {
-        scores(op);
         load_v_operands(vaddr, off1, op);
 #pragma unroll
-        for (int i = 0; i < NSM; i++) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one score MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, NVR / NSM, 0);    // its share of V reads
+        for (int i = 0; i < NSC; i++) score_mfma_and_k(i, op, kaddr, off2, true);
+#pragma unroll
+        for (int i = 0; i < NSC; i++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one score MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);  // its share of LDS reads
         }
       }
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       if (grp == 1) ring_barrier(k);
-      if (grp == 0 && k == 0) barrier_e(true);
       __builtin_amdgcn_sched_barrier(0);
-      // Y(k): K operands of chunk k+2 (for X(k+1); a chunk past the wave's last is
-      // read too and not used), softmax of chunk k+1 (vector ALU)
+      // Y(k), the vector phase: softmax of chunk k+1, and the scalar half of
+      // X(k+1)'s stage request
       if (k + 1 < nok) {
-        load_k_operands(kaddr, off2, op);
         prepare_scores<MB, CAUSAL>(op, k + 1 >= kmask, chunk_key(k + 1), kstop, L, qi, h, c2, acc);
         numerators<MB>(op, c2, acc);
       }
+      req = stage_req(stage_key(k + 1 + NSLOT), sl);
       __builtin_amdgcn_sched_barrier(0);
       if (grp == 0) ring_barrier(k);
     }
