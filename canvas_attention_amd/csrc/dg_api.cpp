@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "dg.h"
@@ -274,6 +275,16 @@ struct Call {
   Mode mode;
 };
 
+// Partial rows [n_units][R][D] at the start of the workspace, then (max, sum) pairs.
+void set_workspace(Call* c, void* workspace) {
+  c->args.part_o = workspace;
+  c->args.part_ml = workspace ? (float*)((char*)workspace + (size_t)c->plan.n_units *
+                                                               c->plan.rows_per_unit *
+                                                               c->shape.head_dim *
+                                                               out_elem_size(c->shape.dtype))
+                              : nullptr;
+}
+
 dg_status prepare(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
                   const int32_t* prefix_len, const dg_kv* kv_new, void* out, void* workspace,
                   size_t ws_bytes, Mode mode, Call* c) {
@@ -328,11 +339,7 @@ dg_status prepare(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
   a.k_append = commit ? kv_cache->k : nullptr;
   a.v_append = commit ? kv_cache->v : nullptr;
   a.out = out;
-  a.part_o = workspace;
-  a.part_ml = workspace ? (float*)((char*)workspace + (size_t)c->plan.n_units *
-                                                           c->plan.rows_per_unit *
-                                                           shape->head_dim * out_elem_size(shape->dtype))
-                        : nullptr;
+  set_workspace(c, workspace);
   a.cap = kv_cache->capacity;
   a.n_heads_q = shape->n_heads_q;
   a.n_heads_kv = shape->n_heads_kv;
@@ -345,10 +352,10 @@ dg_status prepare(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
   return DG_OK;
 }
 
-dg_status launch(const Call& c, void* stream) {
+dg_status launch(const Call& c, void* stream, bool timed = true) {
   hipStream_t st = (hipStream_t)stream;
   const int dt = c.shape.dtype;
-  time_begin(0, st);
+  if (timed) time_begin(0, st);
   int err;
   if (c.mode == kDecode && mfma_path(dt))
     err = dg::launch_decode(c.args, c.plan, dt, c.shape.head_dim, stream);
@@ -358,16 +365,16 @@ dg_status launch(const Call& c, void* stream) {
     err = dg::launch_attn_fp8(c.args, c.plan, c.causal, stream);
   else
     err = dg::launch_attn_f32(c.args, c.plan, c.shape.head_dim, c.causal, stream);
-  time_end(0, st);
+  if (timed) time_end(0, st);
   if (err != 0)
     return fail(DG_ERR_HIP, "attention kernel launch failed: %s",
                 hipGetErrorString((hipError_t)err));
   bool any = false;
   for (int b = 0; b < c.plan.batch; b++) any = any || c.plan.seq[b].n_splits > 1;
   if (any) {
-    time_begin(1, st);
+    if (timed) time_begin(1, st);
     err = dg::launch_merge(c.args, c.plan, c.shape.head_dim, dt != DG_F32, stream);
-    time_end(1, st);
+    if (timed) time_end(1, st);
     if (err != 0)
       return fail(DG_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString((hipError_t)err));
   }
@@ -380,6 +387,36 @@ dg_status launch(const Call& c, void* stream) {
               c.plan.seq[b].n_splits, c.plan.seq[b].split_keys);
     fprintf(stderr, "\n");
   }
+  return DG_OK;
+}
+
+// ------------------------------------------------ no-allocation entry point
+// dg_canvas_attn_noalloc keeps its partial results in this file-scope device
+// array instead of a caller workspace.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` is only a stand-in for the
+// symbol: the device address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = DG_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+dg_status scratch_address(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(DG_ERR_HIP, "device index %d outside 0..63", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r != hipSuccess || !p)
+      return fail(DG_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s",
+                  hipGetErrorString(r));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return DG_OK;
 }
 
@@ -411,6 +448,31 @@ dg_status dg_canvas_attn(const dg_shape* shape, const void* q, const dg_kv* kv_c
                          kCanvasStep, &c);
   if (st) return st;
   return launch(c, stream);
+}
+
+dg_status dg_canvas_attn_noalloc(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
+                                 const int32_t* prefix_len, const dg_kv* kv_canvas, void* out,
+                                 void* stream) {
+  // Validate and plan against a stand-in workspace of the scratch's size (never
+  // dereferenced), so that a call the scratch cannot hold is rejected before any
+  // HIP call; then point the partial results at this device's scratch array.
+  Call c;
+  void* const stand_in = (void*)(uintptr_t)256;
+  dg_status st = prepare(shape, q, kv_cache, prefix_len, kv_canvas, out, stand_in, kScratchBytes,
+                         kCanvasStep, &c);
+  if (st == DG_ERR_WORKSPACE)
+    return fail(DG_ERR_WORKSPACE,
+                "this call needs %zu bytes of partial results, more than the %zu-byte scratch "
+                "of dg_canvas_attn_noalloc (use dg_canvas_attn with a workspace)",
+                plan_workspace(shape, c.plan), kScratchBytes);
+  if (st) return st;
+  void* ws = nullptr;
+  if (plan_workspace(shape, c.plan) > 0) {
+    st = scratch_address(&ws);
+    if (st) return st;
+  }
+  set_workspace(&c, ws);
+  return launch(c, stream, false);
 }
 
 dg_status dg_commit_block(const dg_shape* shape, const void* q_blk, const dg_kv* kv_blk,

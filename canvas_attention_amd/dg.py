@@ -69,6 +69,8 @@ lib.dg_workspace_bytes.argtypes = [_P(DgShape), _i64]
 lib.dg_workspace_bytes.restype = _sz
 lib.dg_canvas_attn.argtypes = [_P(DgShape), _vp, _P(DgKv), _vp, _P(DgKv), _vp, _vp, _sz, _vp]
 lib.dg_canvas_attn.restype = _i32
+lib.dg_canvas_attn_noalloc.argtypes = [_P(DgShape), _vp, _P(DgKv), _vp, _P(DgKv), _vp, _vp]
+lib.dg_canvas_attn_noalloc.restype = _i32
 lib.dg_commit_block.argtypes = [_P(DgShape), _vp, _P(DgKv), _P(DgKv), _vp, _vp, _vp, _sz, _vp]
 lib.dg_commit_block.restype = _i32
 lib.dg_canvas_step_loop.argtypes = [_P(DgShape), _i32, _vp, _i64, _P(DgKv), _i64, _P(DgKv), _vp,
@@ -97,7 +99,8 @@ lib.dg_kernel_timing_samples.argtypes = [_P(ctypes.c_float), _P(ctypes.c_float),
                                          _P(_i32)]
 lib.dg_kernel_timing_samples.restype = _i32
 
-EXPORTS = ["dg_workspace_bytes", "dg_canvas_attn", "dg_commit_block", "dg_canvas_step_loop",
+EXPORTS = ["dg_workspace_bytes", "dg_canvas_attn", "dg_canvas_attn_noalloc", "dg_commit_block",
+           "dg_canvas_step_loop",
            "dg_canvas_sample", "dg_decode_workspace_bytes", "dg_decode_attn",
            "dg_selfcond_workspace_bytes", "dg_self_condition",
            "dg_status_string", "dg_last_error", "dg_kernel_timing_enable",
@@ -233,6 +236,28 @@ def canvas_attn(q, k_cache, v_cache, prefix_len, k_canvas, v_canvas, out=None, w
                             _ptr(workspace), workspace.numel() * workspace.element_size(),
                             _stream(stream))
     _check("dg_canvas_attn", st)
+    return out
+
+
+def canvas_attn_noalloc(q, k_cache, v_cache, prefix_len, k_canvas, v_canvas, out, scale=None,
+                        stream=None, tensor_scales=None):
+    """dg_canvas_attn_noalloc: dg_canvas_attn with its partial results in the
+    library's per-GPU scratch array instead of a workspace; the caller passes
+    `out`, so nothing is allocated on this path."""
+    dt = q.dtype
+    _need(q, "q", dt, 4)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_canvas", k_canvas),
+                    ("v_canvas", v_canvas)):
+        _need(t, name, dt, 4)
+    _need(out, "out", out_dtype(dt), 4)
+    _check_attn(q, k_cache, v_cache, k_canvas, v_canvas, out, ("q", "k_canvas", "v_canvas"))
+    shape = _shape(q, k_cache.shape[2], scale, tensor_scales)
+    cache = DgKv(k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1])
+    canv = DgKv(k_canvas.data_ptr(), v_canvas.data_ptr(), k_canvas.shape[1])
+    st = lib.dg_canvas_attn_noalloc(ctypes.byref(shape), _ptr(q), ctypes.byref(cache),
+                                    _prefix(prefix_len, q.shape[0]), ctypes.byref(canv), _ptr(out),
+                                    _stream(stream))
+    _check("dg_canvas_attn_noalloc", st)
     return out
 
 

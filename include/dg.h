@@ -135,6 +135,27 @@ dg_status dg_canvas_attn(const dg_shape* shape, const void* q, const dg_kv* kv_c
                          void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * dg_canvas_attn without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, result and validation as dg_canvas_attn,
+ * bit for bit, except that the split partial results live in a file-scope
+ * device array of the library of DG_NOALLOC_SCRATCH_BYTES bytes: one copy per
+ * GPU, held from the library's first use on that GPU until the process ends.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the first call on a device looks up that device's scratch address
+ * once.  A call whose partial results exceed the scratch is rejected with
+ * DG_ERR_WORKSPACE before any HIP call (at Hq=16, Hkv=8, D=128 the scratch holds
+ * every batch up to 8 sequences at any prefix length).  Every call on one GPU
+ * shares its scratch, and each call overwrites what the last one left: calls
+ * that overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller.  No kernel timing hooks run on this path.
+ */
+#define DG_NOALLOC_SCRATCH_BYTES (32u << 20)
+dg_status dg_canvas_attn_noalloc(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
+                                 const int32_t* prefix_len, const dg_kv* kv_canvas, void* out,
+                                 void* stream);
+
+/*
  * Block commit (causal encoder of the mechanism section).  Block row i of
  * sequence b attends to cache rows 0..prefix_len[b]-1 and block rows 0..i
  * (diagonal included):

@@ -324,3 +324,24 @@ def test_binding_step_tensors_hold_n_steps(dg):
     t["out"] = torch.zeros(11, 2, 256, 16, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="expected"):
         _check(dg, t, ("q_steps", "k_steps", "v_steps"))
+
+
+def test_noalloc_rejects_before_any_hip_call(dg):
+    """A shape whose partial results exceed the scratch array is refused on the host
+    (fake device pointers, never dereferenced), as are the usual argument errors."""
+    # 63 empty prefixes and one of 8192 rows: 2016 single-split units plus a split
+    # sequence, so every unit writes partial rows (about 71 MB at this shape)
+    big = shape(dg, batch=64)
+    pl = (ctypes.c_int32 * 64)(*([0] * 63 + [8192]))
+    cache = dg.DgKv(FAKE, FAKE, 8192 + 256)
+    canvas = dg.DgKv(FAKE, FAKE, 256)
+    st = dg.lib.dg_canvas_attn_noalloc(ctypes.byref(big), FAKE, ctypes.byref(cache), pl,
+                                       ctypes.byref(canvas), FAKE, None)
+    assert st == -5 and b"scratch" in dg.lib.dg_last_error()
+    one = (ctypes.c_int32 * 1)(100)
+    st = dg.lib.dg_canvas_attn_noalloc(ctypes.byref(shape(dg, head_dim=96)), FAKE,
+                                       ctypes.byref(cache), one, ctypes.byref(canvas), FAKE, None)
+    assert st == -2
+    st = dg.lib.dg_canvas_attn_noalloc(ctypes.byref(shape(dg)), None, ctypes.byref(cache), one,
+                                       ctypes.byref(canvas), FAKE, None)
+    assert st == -1

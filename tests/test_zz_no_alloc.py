@@ -1,0 +1,58 @@
+"""dg_canvas_attn_noalloc (partial results in the library's per-GPU scratch array)
+against dg_canvas_attn (partial results in a caller workspace): the same kernels
+on the same plan, so the outputs must agree bit for bit; also against the oracle
+at the bf16 gate.  Two calls in a row, the second with a smaller input, so the
+second call runs on scratch the first one left behind."""
+import numpy as np
+import pytest
+
+from canvas_attention_amd import synth
+from helpers import TOL_BF16, record, row_err, to_dev, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU machines skip the module
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import canvas_attention_amd.dg as dg  # noqa: E402  (loads libdg.so; raises if missing)
+
+
+def _inputs(seed, L, B, Hq=16, Hkv=8, D=128):
+    L = np.asarray(L, np.int32)
+    kc, vc = synth.cache(seed, L, int(L.max()) + 256, Hkv, D, "bf16")
+    q, kn, vn = synth.canvas(seed, B, Hq, Hkv, D, "bf16")
+    return L, kc, vc, q, kn, vn
+
+
+def test_noalloc_matches_the_workspace_entry_point(oracle_lib):
+    # the second call is smaller: fewer sequences and units, a shorter prefix
+    for seed, L in ((41, [8192, 3000]), (42, [700])):
+        L, kc, vc, q, kn, vn = _inputs(seed, L, len(L))
+        args = (to_dev(q), to_dev(kc), to_dev(vc), L, to_dev(kn), to_dev(vn))
+        ref = dg.canvas_attn(*args)
+        out = torch.empty_like(ref)
+        got = dg.canvas_attn_noalloc(*args, out=out)
+        torch.cuda.synchronize()
+        assert got.data_ptr() == out.data_ptr()
+        assert torch.equal(got, ref), f"L={L.tolist()}: noalloc differs from dg_canvas_attn"
+        err = record(f"noalloc L={L.tolist()}",
+                     row_err(to_host_f64(got), oracle_lib.canvas_attn(q, kc, vc, L, kn, vn)), TOL_BF16)
+        assert err <= TOL_BF16
+
+
+def test_noalloc_rejects_a_call_beyond_its_scratch():
+    """63 empty prefixes and one of 8192 rows: every one of the 2000-odd units then
+    writes partial rows (about 71 MB), more than the scratch holds.  The call is
+    refused on the host with a clear error and the output is left untouched (the
+    tensors' contents do not matter: nothing is launched)."""
+    B, Hq, Hkv, D = 64, 16, 8, 128
+    L = np.array([0] * 63 + [8192], np.int32)
+    z = lambda *s: torch.zeros(*s, dtype=torch.bfloat16, device="cuda")  # noqa: E731
+    args = (z(B, 256, Hq, D), z(B, 8192 + 256, Hkv, D), z(B, 8192 + 256, Hkv, D), L,
+            z(B, 256, Hkv, D), z(B, 256, Hkv, D))
+    out = z(B, 256, Hq, D)
+    with pytest.raises(dg.DgError, match="scratch"):
+        dg.canvas_attn_noalloc(*args, out=out)
+    torch.cuda.synchronize()
+    assert not out.any()
