@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdg.so")
 SOURCES = ["dg_attn_mfma.hip", "dg_attn_f32.hip", "dg_merge.hip", "dg_sample.hip", "dg_selfcond.hip",
-           "dg_api.cpp"]
+           "dg_api.cpp", "dg_plan.cpp"]
 ARCH = "gfx950"
 
 

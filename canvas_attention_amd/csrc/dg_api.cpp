@@ -24,7 +24,14 @@
 namespace {
 
 using dg::AttnArgs;
+using dg::key_granule;
+using dg::make_decode_plan;
+using dg::make_plan;
+using dg::mfma_path;
+using dg::out_elem_size;
+using dg::partial_row_bytes;
 using dg::Plan;
+using dg::plan_workspace;
 
 thread_local std::string g_last_error;
 
@@ -55,17 +62,8 @@ int device_cu_count() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Bytes of one stored input element (q, K, V) and of one output / partial element.
+// Bytes of one stored input element (q, K, V).
 size_t elem_size(int dtype) { return dtype == DG_FP8 ? 1 : dtype == DG_BF16 ? 2 : 4; }
-size_t out_elem_size(int dtype) { return dtype == DG_F32 ? 4 : 2; }
-
-// The matrix-core kernels (bf16 and fp8) against the fp32 vector kernel.
-bool mfma_path(int dtype) { return dtype != DG_F32; }
-
-// Keys per chunk of the kernel a dtype runs on: split boundaries are multiples of it.
-int key_granule(int dtype) { return dtype == DG_FP8 ? 64 : dg::kKeyGranule; }
-
-int rows_per_unit(int dtype) { return mfma_path(dtype) ? dg::kRowsMfma : dg::kRowsF32; }
 
 // Call kinds: the canvas step, the block commit and decode attention.
 enum Mode { kCanvasStep = 0, kCommit = 1, kDecode = 2 };
@@ -124,117 +122,10 @@ int forced_split_keys(int dtype) {
 // (eight waves, two per SIMD), one wave per SIMD for the fp32 kernel.
 int target_units(int dtype) { return device_cu_count() * (mfma_path(dtype) ? 1 : 4); }
 
-// Split-key plan: every unit of every sequence gets about the same number of
-// keys, chosen so that the units fill the device about once.
-void make_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
-  const int R = rows_per_unit(s->dtype);
-  const int G = s->n_heads_q / s->n_heads_kv;
-  const int NRT = dg::kCanvas * G / R;
-  const int per_split = s->n_heads_kv * NRT;  // units per split index
-  int64_t W = 0;
-  for (int b = 0; b < s->batch; b++) W += (int64_t)(prefix_len[b] + dg::kCanvas) * per_split;
-  const int T = target_units(s->dtype);
-  const int gran = key_granule(s->dtype);
-  int64_t kappa = (W + T - 1) / T;
-  kappa = ((kappa + gran - 1) / gran) * gran;
-  kappa = std::max<int64_t>(kappa, mfma_path(s->dtype) ? 256 : 64);
-  const int forced = forced_split_keys(s->dtype);
-  if (forced) kappa = forced;
-  memset(p, 0, sizeof *p);
-  p->batch = s->batch;
-  p->n_q = dg::kCanvas;
-  p->rcp_m = dg::rcp_u32((uint32_t)(dg::kCanvas * G));
-  p->n_rowtiles = NRT;
-  p->rows_per_unit = R;
-  p->g = G;
-  p->rcp_g = dg::rcp_u32((uint32_t)G);
-  p->rcp_nrt = dg::rcp_u32((uint32_t)NRT);
-  int units = 0;
-  for (int b = 0; b < s->batch; b++) {
-    const int64_t K = (int64_t)prefix_len[b] + dg::kCanvas;
-    int S = (int)((K + kappa - 1) / kappa);
-    int64_t sk = (K + S - 1) / S;
-    sk = ((sk + gran - 1) / gran) * gran;
-    S = (int)((K + sk - 1) / sk);
-    p->seq[b].prefix_len = prefix_len[b];
-    p->seq[b].n_splits = S;
-    p->seq[b].split_keys = (int)sk;
-    p->seq[b].unit_base = units;
-    p->seq[b].rcp_s = dg::rcp_u32((uint32_t)S);
-    p->seq[b].rcp_snrt = dg::rcp_u32((uint32_t)(S * NRT));
-    units += S * per_split;
-  }
-  p->n_units = units;
-}
-
-// Decode plan: tiles of R packed rows (32 on the matrix cores, 64 for fp32), and
-// key splits sized so that the units fill the device once.  With P = B*Hkv*NRT
-// units per split index, splits of kappa >= W / (T - P) keys give at most
-// W/kappa + P <= T units (each sequence adds at most one partial split per head
-// and tile), so no second round of workgroups waits behind the first.
-int decode_rows(int dtype) { return mfma_path(dtype) ? dg::kDecodeRows : dg::kRowsF32; }
-
 int decode_target_units(int dtype) {
   // the matrix-core decode kernel takes one workgroup per CU (its LDS rings); the
   // fp32 kernel runs one wave per unit, four per CU
   return device_cu_count() * (mfma_path(dtype) ? 1 : 4);
-}
-
-void make_decode_plan(const dg_shape* s, const int32_t* prefix_len, Plan* p) {
-  const int nq = s->n_canvas;
-  const int R = decode_rows(s->dtype);
-  const int G = s->n_heads_q / s->n_heads_kv;
-  const int NRT = (nq * G + R - 1) / R;
-  const int per_split = s->n_heads_kv * NRT;
-  int64_t W = 0;
-  for (int b = 0; b < s->batch; b++) W += (int64_t)(prefix_len[b] + nq) * per_split;
-  const int64_t T = decode_target_units(s->dtype);
-  const int64_t P = (int64_t)s->batch * per_split;
-  const int gran = key_granule(s->dtype);
-  const int64_t avail = T > 2 * P ? T - P : T;
-  int64_t kappa = (W + avail - 1) / avail;
-  kappa = ((kappa + gran - 1) / gran) * gran;
-  // at least one chunk per wave of the unit
-  kappa = std::max<int64_t>(kappa, mfma_path(s->dtype) ? (int64_t)dg::kDecodeWaves * gran : 64);
-  const int forced = forced_split_keys(s->dtype);
-  if (forced) kappa = forced;
-  memset(p, 0, sizeof *p);
-  p->batch = s->batch;
-  p->n_q = nq;
-  p->rcp_m = dg::rcp_u32((uint32_t)(nq * G));
-  p->n_rowtiles = NRT;
-  p->rows_per_unit = R;
-  p->g = G;
-  p->rcp_g = dg::rcp_u32((uint32_t)G);
-  p->rcp_nrt = dg::rcp_u32((uint32_t)NRT);
-  int64_t units = 0;
-  for (int b = 0; b < s->batch; b++) {
-    const int64_t K = (int64_t)prefix_len[b] + nq;
-    int64_t S = (K + kappa - 1) / kappa;
-    int64_t sk = (K + S - 1) / S;
-    sk = ((sk + gran - 1) / gran) * gran;
-    S = (K + sk - 1) / sk;
-    p->seq[b].prefix_len = prefix_len[b];
-    p->seq[b].n_splits = (int)S;
-    p->seq[b].split_keys = (int)sk;
-    p->seq[b].unit_base = (int)std::min<int64_t>(units, INT32_MAX);
-    p->seq[b].rcp_s = dg::rcp_u32((uint32_t)S);
-    p->seq[b].rcp_snrt = dg::rcp_u32((uint32_t)(S * NRT));
-    units += S * per_split;
-  }
-  p->n_units = (int)std::min<int64_t>(units, INT32_MAX);
-}
-
-// Bytes of one partial row: the normalised output (bf16 or fp32) plus max and sum.
-size_t partial_row_bytes(const dg_shape* s) {
-  return (size_t)s->head_dim * out_elem_size(s->dtype) + 2 * sizeof(float);
-}
-
-size_t plan_workspace(const dg_shape* s, const Plan& p) {
-  bool any = false;
-  for (int b = 0; b < p.batch; b++) any = any || p.seq[b].n_splits > 1;
-  if (!any) return 0;
-  return (size_t)p.n_units * p.rows_per_unit * partial_row_bytes(s);
 }
 
 // ------------------------------------------------------------ kernel timing
@@ -319,9 +210,11 @@ dg_status prepare(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
   c->causal = commit;
   c->mode = mode;
   if (mode == kDecode)
-    make_decode_plan(shape, prefix_len, &c->plan);
+    make_decode_plan(shape, prefix_len, decode_target_units(shape->dtype),
+                     forced_split_keys(shape->dtype), &c->plan);
   else
-    make_plan(shape, prefix_len, &c->plan);
+    make_plan(shape, prefix_len, target_units(shape->dtype), forced_split_keys(shape->dtype),
+              &c->plan);
   // unit and row indices stay below 2^16, which keeps every kernel division n/d with
   // n*d < 2^32 (the reciprocal-multiplier form is exact there)
   if (c->plan.n_units >= dg::kMaxUnits)
@@ -427,17 +320,8 @@ extern "C" {
 size_t dg_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len) {
   if (check_shape(shape) != DG_OK || max_prefix_len < 0 || max_prefix_len > INT32_MAX / 2)
     return 0;
-  // The natural plan never exceeds T + B*Hkv*NRT units whatever the prefixes.
-  const int R = rows_per_unit(shape->dtype);
-  const int G = shape->n_heads_q / shape->n_heads_kv;
-  const int NRT = dg::kCanvas * G / R;
-  int64_t units = (int64_t)target_units(shape->dtype) + (int64_t)shape->batch * shape->n_heads_kv * NRT;
-  const int forced = forced_split_keys(shape->dtype);
-  if (forced) {
-    const int64_t S = (max_prefix_len + dg::kCanvas + forced - 1) / forced;
-    units = std::max<int64_t>(units, S * shape->batch * shape->n_heads_kv * NRT);
-  }
-  return (size_t)units * R * partial_row_bytes(shape);
+  return dg::workspace_bound(shape, max_prefix_len, target_units(shape->dtype),
+                             forced_split_keys(shape->dtype));
 }
 
 dg_status dg_canvas_attn(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
@@ -489,17 +373,8 @@ size_t dg_decode_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len) 
   if (check_shape(shape, kDecode) != DG_OK || max_prefix_len < 0 ||
       max_prefix_len > INT32_MAX / 2)
     return 0;
-  // the decode plan never exceeds T + B*Hkv*NRT units (see make_decode_plan)
-  const int nq = shape->n_canvas, R = decode_rows(shape->dtype);
-  const int G = shape->n_heads_q / shape->n_heads_kv;
-  const int64_t per_split = (int64_t)shape->n_heads_kv * ((nq * G + R - 1) / R);
-  int64_t units = decode_target_units(shape->dtype) + (int64_t)shape->batch * per_split;
-  const int forced = forced_split_keys(shape->dtype);
-  if (forced) {
-    const int64_t S = (max_prefix_len + nq + forced - 1) / forced;
-    units = std::max<int64_t>(units, S * shape->batch * per_split);
-  }
-  return (size_t)units * R * partial_row_bytes(shape);
+  return dg::decode_workspace_bound(shape, max_prefix_len, decode_target_units(shape->dtype),
+                                    forced_split_keys(shape->dtype));
 }
 
 dg_status dg_decode_attn(const dg_shape* shape, const void* q, const dg_kv* kv_new,

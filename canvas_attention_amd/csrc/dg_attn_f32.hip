@@ -18,11 +18,6 @@
 namespace dg {
 namespace {
 
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int x = bid % kNumXcd, j = bid / kNumXcd;
-  return x * (n / kNumXcd) + min(x, n % kNumXcd) + j;
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, Plan plan) {
   constexpr int R = kRowsF32;
@@ -33,12 +28,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, Plan plan) {
 
   const int lane = threadIdx.x;
   const int U = xcd_remap(blockIdx.x, gridDim.x);
-  int b = 0;
-  for (int i = 1; i < plan.batch; i++)
-    if (U >= plan.seq[i].unit_base) b = i;
-  const SeqPlan sp = plan.seq[b];
-  const int local = U - sp.unit_base, NRT = plan.n_rowtiles;
-  const int g = local / (sp.n_splits * NRT), s = (local / NRT) % sp.n_splits, rt = local % NRT;
+  SeqPlan sp;
+  const Unit u = decode_unit(plan, U, sp);
+  const int b = u.b, g = u.g, s = u.s, rt = u.rt, NRT = plan.n_rowtiles;
   const int L = sp.prefix_len;
   const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = Hq / Hkv;
   const int row0 = rt * R;

@@ -120,43 +120,7 @@ __device__ __forceinline__ int swz8(int r) { return 2 * ((r >> 1) & 3) | ((r >> 
 // 32t + 16h + i, which two 8-row transposing reads match on the V side.
 __device__ __forceinline__ int kperm8(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
-  // range of logical units so units that share K/V tiles share an L2.
-  const int x = bid % kNumXcd, j = bid / kNumXcd;
-  return x * (n / kNumXcd) + min(x, n % kNumXcd) + j;
-}
-
-struct Unit {
-  int b, g, s, rt;
-};
-
-// floor(n / d) from the host's reciprocal multiplier m = rcp_u32(d), valid for n*d < 2^32
-// (m = 0 encodes d = 1); written without a branch so that the scalar loads around it
-// stay in one basic block and are issued together
-__device__ __forceinline__ int div_rcp(int n, uint32_t m) {
-  return (int)__umulhi((uint32_t)n, m) + (m == 0u ? n : 0);
-}
-
-// Unit U of the launch and the plan of its sequence.  Sequence 0's entry is read
-// together with the plan header; a unit of a later sequence costs one more scalar
-// round trip.
-__device__ __forceinline__ Unit decode_unit(const Plan& p, int U, SeqPlan& sp) {
-  sp = p.seq[0];
-  int b = 0;
-  for (int i = 1; i < p.batch; i++)
-    if (U >= p.seq[i].unit_base) b = i;
-  if (b != 0) sp = p.seq[b];
-  const int local = U - sp.unit_base;
-  const int S = sp.n_splits, NRT = p.n_rowtiles;
-  const int q = div_rcp(local, p.rcp_nrt);  // local / NRT
-  Unit u;
-  u.b = b;
-  u.g = div_rcp(local, sp.rcp_snrt);
-  u.s = q - div_rcp(q, sp.rcp_s) * S;
-  u.rt = local - q * NRT;
-  return u;
-}
+// Work units come from the plan: xcd_remap, decode_unit and div_rcp (dg_plan.h).
 
 __device__ __forceinline__ float partner_max(float x) {
   // lanes l and l^32 exchange through v_permlane32_swap; max of both halves

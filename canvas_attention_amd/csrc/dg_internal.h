@@ -1,61 +1,13 @@
-// dg_internal.h -- types shared by the host API and the gfx950 kernels of libdg.
-//
-// Work decomposition ("split-key plan").  For every sequence b the key space
-// of one call is the concatenation [cache rows 0..L_b-1 ; new rows 0..n_q-1]
-// (the canvas or block of 256 rows, or the 1..16 tokens of a decode call).
-// Query rows of one kv head are packed: packed row p = i*G + hh is new row i of
-// query head g*G + hh, so the G query heads sharing kv head g form one matrix of
-// n_q*G rows.  A work unit is (sequence b, kv head g, key
-// split s, row tile rt): rows [rt*R, rt*R+R) of that packed matrix against keys
-// [s*split_keys, min((s+1)*split_keys, end)).  Each unit writes one partial
-// result (normalised output rows plus log2-domain max and sum) that a merge
-// kernel combines; a sequence with a single split writes its output directly.
+// dg_internal.h -- types shared by the host API and the gfx950 kernels of libdg
+// (the split-key plan and its unit decode are in dg_plan.h).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "dg.h"
+#include "dg_plan.h"
 
 namespace dg {
-
-constexpr int kCanvas = DG_N_CANVAS;
-constexpr int kMaxBatch = DG_MAX_BATCH;
-constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
-
-struct SeqPlan {
-  int32_t prefix_len;  // L_b
-  int32_t n_splits;    // S_b >= 1
-  int32_t split_keys;  // keys per split (multiple of 32); the last split may be shorter
-  int32_t unit_base;   // first logical unit index of this sequence
-  uint32_t rcp_s;      // div_rcp multipliers of S_b and S_b * NRT
-  uint32_t rcp_snrt;
-};
-
-// Reciprocal multiplier for floor(n / d) when n * d < 2^32: with m = floor(2^32/d) + 1,
-// floor(n*m / 2^32) = floor(n/d), because the excess n*(m - 2^32/d)/2^32 < n/2^32 < 1/d
-// cannot reach the next multiple of d.  d = 1 is encoded as m = 0.  The kernels divide
-// by per-call values (heads per kv head, splits, row tiles) this way: a hardware-free
-// integer division costs tens of dependent instructions before the first load.
-inline uint32_t rcp_u32(uint32_t d) { return d <= 1 ? 0u : (uint32_t)((1ull << 32) / d + 1); }
-
-// Packed rows per unit of the matrix-core canvas/commit kernels (bf16 and fp8):
-// eight waves of 32 rows, four row groups x two key groups.
-constexpr int kRowsMfma = 128;
-
-struct Plan {
-  int32_t batch;
-  int32_t n_q;          // query rows per sequence and head: 256 (canvas, commit) or the
-                        // decode call's new tokens (1..DG_MAX_DECODE)
-  uint32_t rcp_m;       // div_rcp multiplier of n_q * G (packed rows per kv head)
-  int32_t n_units;      // total logical units = grid size of the attention kernel (< 2^16)
-  int32_t n_rowtiles;   // NRT = ceil(n_q*G / R)
-  int32_t rows_per_unit;// R
-  int32_t g;            // G = query heads per kv head
-  uint32_t rcp_g;       // div_rcp multipliers of G and NRT
-  uint32_t rcp_nrt;
-  SeqPlan seq[kMaxBatch];
-};
-constexpr int kMaxUnits = 1 << 16;
 
 struct AttnArgs {
   const void* q;        // [B][n_q][Hq][D]
@@ -127,14 +79,5 @@ int launch_decode(const AttnArgs& a, const Plan& p, int dtype, int head_dim, voi
 int launch_selfcond(const SelfcondArgs& a, void* stream);
 // contraction rows per split of a self-conditioning product (a multiple of 32)
 int selfcond_splits(int K, int N, int M, int cus);
-
-// Rows per unit of the fp32 kernel and the key granule of every kernel.
-constexpr int kRowsF32 = 64;
-constexpr int kKeyGranule = 32;
-
-// Decode kernel (dg_attn_mfma.hip): 32 packed rows per unit, kDecodeWaves waves that
-// stream their own chunks; one workgroup per CU.
-constexpr int kDecodeRows = 32;
-constexpr int kDecodeWaves = 4;
 
 }  // namespace dg

@@ -19,18 +19,9 @@
 namespace dg {
 namespace {
 
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  // Same dealing as the attention kernel: contiguous logical blocks on one XCD,
-  // so the rows of a kv head are merged on the XCD whose L2 holds its partials.
-  const int x = bid % kNumXcd, j = bid / kNumXcd;
-  return x * (n / kNumXcd) + min(x, n % kNumXcd) + j;
-}
-
-// floor(n / d) from the host's reciprocal multiplier m = rcp_u32(d), valid for
-// n*d < 2^32 (m = 0 encodes d = 1)
-__device__ __forceinline__ int div_rcp(int n, uint32_t m) {
-  return (int)__umulhi((uint32_t)n, m) + (m == 0u ? n : 0);
-}
+// Blocks are dealt like the attention kernel's units (xcd_remap, dg_plan.h):
+// contiguous logical blocks on one XCD, so the rows of a kv head are merged on the
+// XCD whose L2 holds its partials.
 
 // Partial rows are bf16 for the bf16 path and fp32 for the fp32 path; each thread
 // combines 8 (bf16) or 4 (fp32) adjacent head_dim elements of one row.  Block
@@ -56,7 +47,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, Plan plan) {
   const int rsh = __builtin_ctz((unsigned)plan.rows_per_unit), NRT = plan.n_rowtiles;
   const int rt = p >> rsh, pr = p & (plan.rows_per_unit - 1);
   const int R = plan.rows_per_unit;
-  const int u0 = sp.unit_base + g * sp.n_splits * NRT + rt;
+  const int u0 = unit_index(plan, sp, g, 0, rt);  // split s is u0 + s*NRT
 
   // Splits are visited in batches of 8 with all loads of a batch in flight at
   // once; a running max keeps the weights bounded (partials carry finite maxima).
@@ -146,7 +137,7 @@ __global__ __launch_bounds__(256) void merge_dec_kernel(AttnArgs a, Plan plan) {
     g = div_rcp(rem, plan.rcp_m);
     p = rem - g * M;
     const int rt = p >> 5, pr = p & 31;
-    const int u0 = sp.unit_base + g * S * NRT + rt;
+    const int u0 = unit_index(plan, sp, g, 0, rt);  // split s is u0 + s*NRT
     for (int s0 = sg; s0 < S; s0 += 8 * SG) {
       float2 ml[8];
       uint4 v[8];

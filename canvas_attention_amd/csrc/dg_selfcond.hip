@@ -57,11 +57,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const LDS_AS char*)p;
 }
 
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int x = bid % kNumXcd, j = bid / kNumXcd;
-  return x * (n / kNumXcd) + min(x, n % kNumXcd) + j;
-}
-
 // NL (1 or 2) global_load_lds_dwordx4 from scalar base sb + lane offset vo[e] +
 // 1024e into LDS at m0 + 1024e + 16*lane (the instruction offset moves both).
 template <int NL>
