@@ -89,11 +89,12 @@ def traffic_file(dtype):
 # The attention kernels' counted traffic also depends on the split plan (dg_api.cpp
 # sets how many partial rows a launch writes) and on the merge that reads them.
 KERNEL_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
-                  for f in ("dg_attn_mfma.hip", "dg_internal.h", "dg_api.cpp", "dg_merge.hip")]
+                  for f in ("dg_attn_mfma.hip", "dg_internal.h", "dg_plan.h", "dg_plan.cpp",
+                            "dg_api.cpp", "dg_merge.hip")]
 SAMPLER_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
-                   for f in ("dg_sample.hip", "dg_internal.h")]
+                   for f in ("dg_sample.hip", "dg_internal.h", "dg_plan.h")]
 SELFCOND_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
-                    for f in ("dg_selfcond.hip", "dg_internal.h")]
+                    for f in ("dg_selfcond.hip", "dg_internal.h", "dg_plan.h")]
 # the decode kernel shares its source file with the canvas kernels
 
 
@@ -219,8 +220,8 @@ def summarize_mfma(pass1_dir, pass2_dir, trace_txt, dtype="bf16"):
     c = {**per_dispatch(pass1_dir), **per_dispatch(pass2_dir)}
     avg_us = None
     for line in open(trace_txt):
-        if ATTN_KERNEL in line:
-            avg_us = float(line.split()[1])
+        if ATTN_KERNEL in line and "L=131072 leg" not in line and not line.startswith("#"):
+            avg_us = float(line.split()[1])  # the L=8192 leg line, when present, comes last
     busy = c["SQ_VALU_MFMA_BUSY_CYCLES"][0] / 1024.0  # per SIMD (256 CUs x 4)
     mops = c[MOPS_COUNTER[dtype]][0]
     tag = PROFILE_TAG[dtype]
@@ -279,6 +280,19 @@ def summarize_trace(stats_csv, out_txt, dtype="bf16", sampler=False, decode=None
         lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.3f} "
                      f"{float(r['MinNs']) / 1e3:10.3f} {float(r['MaxNs']) / 1e3:10.3f} "
                      f"{float(r['Percentage']):9.2f}  {r['Name'][:110]}")
+    # The default run times the same canvas kernel at L=8192 and (its long_context
+    # object) at L=131072; the per-dispatch trace separates the two legs by launch
+    # time (about 20-30 us against 250-370 us).
+    trace_csv = os.path.join(os.path.dirname(stats_csv), "run_kernel_trace.csv")
+    if tag == "bf16" and os.path.exists(trace_csv):
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                for r in csv.DictReader(open(trace_csv)) if ATTN_KERNELS["bf16"] in r["Kernel_Name"]]
+        lines.append("# attn_bf16_kernel<128, false> by leg (per-dispatch trace, split at 100 us):")
+        for leg, sel in (("L=8192", [d for d in durs if d < 100.0]),
+                         ("L=131072", [d for d in durs if d >= 100.0])):
+            if sel:
+                lines.append(f"{len(sel):7d} {sum(sel) / len(sel):10.3f} {min(sel):10.3f} "
+                             f"{max(sel):10.3f} {'':>9}  attn_bf16_kernel<128, false> {leg} leg")
     with open(out_txt, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
