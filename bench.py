@@ -664,7 +664,8 @@ def measure_selfcond(reps=20):
     Median per call (torch events on the launch stream) and per kernel (the
     library's events: the embedding product and the softmax pass).  The embedding
     product's algorithmic bytes are E and the softmax weights (bf16) once; its
-    algorithmic FLOP 2*256*V*d."""
+    algorithmic FLOP 2*256*V*d.  The call's algorithmic bytes are the logits, E,
+    W1, W2 and z once."""
     import torch
     import canvas_attention_amd.dg as dg
     from canvas_attention_amd import synth
@@ -697,8 +698,11 @@ def measure_selfcond(reps=20):
     flop = 2.0 * M * V * d
     gbs = nbytes / (gemm_us * 1e-6) / 1e9
     tfl = flop / (gemm_us * 1e-6) / 1e12
+    call_bytes = M * V * 2 + V * d * 2 + 2 * d * h * 2 + M * d * 2
     return {"batch": B, "vocab": V, "d_model": d, "d_hidden": h, "call_us_median": round(call_us, 2),
             "positions_per_s": round(M / (call_us * 1e-6), 1),
+            "call_GBps": round(call_bytes / (call_us * 1e-6) / 1e9, 1),
+            "call_hbm_frac": round(call_bytes / (call_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "kernels_us": {"embedding_product": round(gemm_us, 2), "softmax": round(soft_us, 2)},
             "softmax_GBps": round(2 * M * V * 2 / (soft_us * 1e-6) / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
