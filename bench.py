@@ -86,11 +86,11 @@ def traffic_file(dtype):
 # (FETCH_SIZE and WRITE_SIZE per dispatch, calibrated against a plain copy of
 # known size) recorded in a profile file together with a hash of the kernel
 # source; it is reported only while the source still matches.
-# The attention kernels' counted traffic also depends on the split plan (dg_api.cpp
+# The attention kernels' counted traffic also depends on the split plan (dg_plan.cpp
 # sets how many partial rows a launch writes) and on the merge that reads them.
 KERNEL_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
                   for f in ("dg_attn_mfma.hip", "dg_internal.h", "dg_plan.h", "dg_plan.cpp",
-                            "dg_api.cpp", "dg_merge.hip")]
+                            "dg_merge.hip")]
 SAMPLER_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)
                    for f in ("dg_sample.hip", "dg_internal.h", "dg_plan.h")]
 SELFCOND_SOURCES = [os.path.join(ROOT, "canvas_attention_amd", "csrc", f)

@@ -295,15 +295,27 @@ __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[64] = {};
 
-dg_status scratch_address(void** out) {
+// The scratch address on the GPU that `stream` belongs to (the current device for
+// the null stream), looked up once per device with that device current.
+dg_status scratch_address(void* stream, void** out) {
   int dev = -1;
-  const hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
   if (dev < 0 || dev >= 64) return fail(DG_ERR_HIP, "device index %d outside 0..63", dev);
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(DG_ERR_HIP, "hipSetDevice(%d) failed: %s", dev, hipGetErrorString(e));
     void* p = nullptr;
     const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      e = hipSetDevice(cur);
+      if (e != hipSuccess)
+        return fail(DG_ERR_HIP, "hipSetDevice(%d) failed: %s", cur, hipGetErrorString(e));
+    }
     if (r != hipSuccess || !p)
       return fail(DG_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s",
                   hipGetErrorString(r));
@@ -352,7 +364,7 @@ dg_status dg_canvas_attn_noalloc(const dg_shape* shape, const void* q, const dg_
   if (st) return st;
   void* ws = nullptr;
   if (plan_workspace(shape, c.plan) > 0) {
-    st = scratch_address(&ws);
+    st = scratch_address(stream, &ws);
     if (st) return st;
   }
   set_workspace(&c, ws);

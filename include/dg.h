@@ -140,7 +140,9 @@ dg_status dg_canvas_attn(const dg_shape* shape, const void* q, const dg_kv* kv_c
  * forbid hipMalloc).  Same arguments, result and validation as dg_canvas_attn,
  * bit for bit, except that the split partial results live in a file-scope
  * device array of the library of DG_NOALLOC_SCRATCH_BYTES bytes: one copy per
- * GPU, held from the library's first use on that GPU until the process ends.
+ * GPU, held from the library's first use on that GPU until the process ends; a
+ * call uses the copy of the GPU its stream belongs to (the current device for
+ * the null stream).
  * The call allocates nothing (no hipMalloc, hipFree or allocating library
  * routine); the first call on a device looks up that device's scratch address
  * once.  A call whose partial results exceed the scratch is rejected with
