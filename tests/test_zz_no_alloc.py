@@ -56,3 +56,36 @@ def test_noalloc_rejects_a_call_beyond_its_scratch():
         dg.canvas_attn_noalloc(*args, out=out)
     torch.cuda.synchronize()
     assert not out.any()
+
+
+def test_noalloc_replayed_from_a_captured_graph():
+    """The callers this entry point is for include code under HIP graph capture:
+    captured once, the call is replayed three times with other eager launches of
+    the library (which also use the scratch's GPU) and synchronizations between
+    the replays; every replay must equal the eager workspace call bit for bit."""
+    L, kc, vc, q, kn, vn = _inputs(43, [3000], 1)
+    args = (to_dev(q), to_dev(kc), to_dev(vc), L, to_dev(kn), to_dev(vn))
+    ref = dg.canvas_attn(*args)
+    out = torch.empty_like(ref)
+    dg.canvas_attn_noalloc(*args, out=out)  # first call on the device: scratch address lookup
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    L2, kc2, vc2, q2, kn2, vn2 = _inputs(44, [5000], 1)
+    other = (to_dev(q2), to_dev(kc2), to_dev(vc2), L2, to_dev(kn2), to_dev(vn2))
+    ref2 = dg.canvas_attn(*other)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            dg.canvas_attn_noalloc(*args, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        # eager work between replays, on the same scratch: another no-allocation call
+        got2 = dg.canvas_attn_noalloc(*other, out=torch.empty_like(ref2))
+        torch.cuda.synchronize()
+        assert torch.equal(got2, ref2), f"replay {rep}: eager call between replays differs"
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs from the eager call"
