@@ -9,20 +9,15 @@
 
 namespace dg {
 
-void make_plan(const dg_shape* s, const int32_t* prefix_len, int target_units,
-               int forced_split_keys, Plan* p) {
+namespace {
+
+// The canvas plan for split size kappa (a multiple of the key granule).
+void fill_plan(const dg_shape* s, const int32_t* prefix_len, int64_t kappa, Plan* p) {
   const int R = rows_per_unit(s->dtype);
   const int G = s->n_heads_q / s->n_heads_kv;
   const int NRT = kCanvas * G / R;
   const int per_split = s->n_heads_kv * NRT;  // units per split index
-  int64_t W = 0;
-  for (int b = 0; b < s->batch; b++) W += (int64_t)(prefix_len[b] + kCanvas) * per_split;
-  const int64_t T = std::max(target_units, 1);
   const int gran = key_granule(s->dtype);
-  int64_t kappa = (W + T - 1) / T;
-  kappa = ((kappa + gran - 1) / gran) * gran;
-  kappa = std::max<int64_t>(kappa, mfma_path(s->dtype) ? 256 : 64);
-  if (forced_split_keys > 0) kappa = forced_split_keys;
   memset(p, 0, sizeof *p);
   p->batch = s->batch;
   p->n_q = kCanvas;
@@ -48,6 +43,67 @@ void make_plan(const dg_shape* s, const int32_t* prefix_len, int target_units,
     units += S * per_split;
   }
   p->n_units = (int)std::min<int64_t>(units, INT32_MAX);
+}
+
+// Keys of the plan's longest unit.
+int64_t longest_unit(const dg_shape* s, const int32_t* prefix_len, const Plan& p) {
+  int64_t m = 0;
+  for (int b = 0; b < s->batch; b++)
+    m = std::max<int64_t>(m, std::min<int64_t>(p.seq[b].split_keys, (int64_t)prefix_len[b] + kCanvas));
+  return m;
+}
+
+}  // namespace
+
+// Split size: the one that fills the device about once, kappa = W/T (W the
+// summed keys of all units, T the units that fill the device once).  Each
+// sequence rounds its own splits up, so a ragged batch can come out with more
+// than T units and spill into a second, mostly idle round of workgroups.  Then
+// split sizes aiming at 2 .. kMaxRounds rounds are weighed too, by the cost of
+// the longest unit (the tail the greedy dispatch cannot fill) plus kRoundKeys
+// per round of workgroups (the prologue and epilogue each round repeats).  The
+// choice depends only on the shape, the prefixes and the device, so every entry
+// point computes the same split plan for the same call.  The constants come
+// from the 8-sequence ragged batch (prefixes 2047..32038, L = 8192-class units
+// of the bf16 kernel): over split sizes of 2464..32320 keys its step time fits
+// 283 us + 0.0049 us per key of the longest unit + 9.1 us per round within 11 us.
+constexpr int64_t kRoundKeys = 1800;
+
+void make_plan(const dg_shape* s, const int32_t* prefix_len, int target_units,
+               int forced_split_keys, Plan* p) {
+  const int R = rows_per_unit(s->dtype);
+  const int G = s->n_heads_q / s->n_heads_kv;
+  const int per_split = s->n_heads_kv * (kCanvas * G / R);
+  int64_t W = 0;
+  for (int b = 0; b < s->batch; b++) W += (int64_t)(prefix_len[b] + kCanvas) * per_split;
+  const int64_t T = std::max(target_units, 1);
+  const int gran = key_granule(s->dtype);
+  const int64_t floor_keys = mfma_path(s->dtype) ? 256 : 64;
+  if (forced_split_keys > 0) {
+    fill_plan(s, prefix_len, forced_split_keys, p);
+    return;
+  }
+  auto kappa_for = [&](int64_t rounds) {
+    int64_t k = (W + rounds * T - 1) / (rounds * T);
+    k = ((k + gran - 1) / gran) * gran;
+    return std::max<int64_t>(k, floor_keys);
+  };
+  fill_plan(s, prefix_len, kappa_for(1), p);
+  if (p->n_units <= T) return;
+  auto cost = [&](const Plan& c) {
+    return longest_unit(s, prefix_len, c) + kRoundKeys * ((c.n_units + T - 1) / T);
+  };
+  int64_t best = cost(*p);
+  Plan c;
+  for (int rounds = 2; rounds <= kMaxRounds; rounds++) {
+    fill_plan(s, prefix_len, kappa_for(rounds), &c);
+    if (c.n_units >= kMaxUnits) continue;
+    const int64_t cc = cost(c);
+    if (cc < best) {
+      best = cc;
+      *p = c;
+    }
+  }
 }
 
 // With P = B*Hkv*NRT units per split index, splits of kappa >= W / (T - P) keys
@@ -109,15 +165,15 @@ size_t plan_workspace(const dg_shape* s, const Plan& p) {
   return (size_t)p.n_units * p.rows_per_unit * partial_row_bytes(s);
 }
 
-// The natural plan never exceeds T + B*Hkv*NRT units whatever the prefixes: each
-// sequence has at most K_b/kappa + 1 splits and kappa >= W/T.
+// A plan aiming at r rounds never exceeds r*T + B*Hkv*NRT units whatever the
+// prefixes: each sequence has at most K_b/kappa + 1 splits and kappa >= W/(r*T).
 size_t workspace_bound(const dg_shape* s, int64_t max_prefix_len, int target_units,
                        int forced_split_keys) {
   const int R = rows_per_unit(s->dtype);
   const int G = s->n_heads_q / s->n_heads_kv;
   const int NRT = kCanvas * G / R;
   const int64_t per_split = (int64_t)s->n_heads_kv * NRT;
-  int64_t units = (int64_t)std::max(target_units, 1) + (int64_t)s->batch * per_split;
+  int64_t units = (int64_t)kMaxRounds * std::max(target_units, 1) + (int64_t)s->batch * per_split;
   if (forced_split_keys > 0) {
     const int64_t S = (max_prefix_len + kCanvas + forced_split_keys - 1) / forced_split_keys;
     units = std::max<int64_t>(units, S * s->batch * per_split);

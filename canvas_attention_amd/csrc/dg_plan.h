@@ -136,7 +136,10 @@ inline int decode_rows(int dtype) { return mfma_path(dtype) ? kDecodeRows : kRow
 inline size_t out_elem_size(int dtype) { return dtype == DG_F32 ? 4 : 2; }
 
 // Canvas step and commit: every unit of every sequence gets about the same number
-// of keys, chosen so that the units fill the device about once.
+// of keys, chosen so that the units fill the device about once; a ragged batch
+// whose plan would spill into a partial second round of workgroups may take a
+// smaller split size that aims at up to kMaxRounds full rounds (dg_plan.cpp).
+constexpr int kMaxRounds = 4;
 void make_plan(const dg_shape* s, const int32_t* prefix_len, int target_units,
                int forced_split_keys, Plan* p);
 // Decode: tiles of R packed rows and key splits sized so that the units fill the
@@ -147,7 +150,8 @@ void make_decode_plan(const dg_shape* s, const int32_t* prefix_len, int target_u
 size_t partial_row_bytes(const dg_shape* s);
 // Workspace a plan's partial rows take (0 when every sequence has one split).
 size_t plan_workspace(const dg_shape* s, const Plan& p);
-// Workspace that covers every plan of this shape with prefixes up to max_prefix_len.
+// Workspace that covers every plan of this shape with prefixes up to max_prefix_len
+// (the canvas bound allows for plans of up to kMaxRounds rounds).
 size_t workspace_bound(const dg_shape* s, int64_t max_prefix_len, int target_units,
                        int forced_split_keys);
 size_t decode_workspace_bound(const dg_shape* s, int64_t max_prefix_len, int target_units,

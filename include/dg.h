@@ -111,7 +111,10 @@ typedef struct {
  * Workspace bytes that any call with this shape and every prefix_len[b] <=
  * max_prefix_len needs (partial results of the split-key plan).  Returns 0 for
  * an invalid shape.  Sizing once for the largest prefix a caller will reach
- * makes one workspace serve a whole generation.
+ * makes one workspace serve a whole generation.  The plan itself depends only on
+ * the shape, the prefix lengths and the device: about one unit of work per CU,
+ * or, for a ragged batch whose units would spill into a partial second round of
+ * workgroups, a smaller split that fills up to four rounds.
  */
 size_t dg_workspace_bytes(const dg_shape* shape, int64_t max_prefix_len);
 
@@ -152,7 +155,7 @@ dg_status dg_canvas_attn(const dg_shape* shape, const void* q, const dg_kv* kv_c
  * that overlap on one GPU (other streams, other host threads) race and must be
  * ordered by the caller.  No kernel timing hooks run on this path.
  */
-#define DG_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define DG_NOALLOC_SCRATCH_BYTES (48u << 20)
 dg_status dg_canvas_attn_noalloc(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
                                  const int32_t* prefix_len, const dg_kv* kv_canvas, void* out,
                                  void* stream);

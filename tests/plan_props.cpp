@@ -69,6 +69,21 @@ static bool check_plan(const Case& c, long* n_units_seen) {
   else
     make_plan(&s, c.L.data(), c.T, c.forced, &p);
   if (p.n_units >= kMaxUnits) return true;  // refused by the API before any launch
+  if (!c.decode && c.forced == 0) {
+    // a plan that fits one round of workgroups is the split size W/T itself
+    int64_t W = 0;
+    for (int b = 0; b < s.batch; b++) W += (int64_t)(c.L[b] + kCanvas);
+    const int64_t per = (int64_t)s.n_heads_kv * (kCanvas * (s.n_heads_q / s.n_heads_kv) /
+                                                 rows_per_unit(s.dtype));
+    if (p.n_units <= c.T) {
+      const int gran = key_granule(s.dtype);
+      int64_t kappa = (W * per + c.T - 1) / c.T;
+      kappa = std::max<int64_t>(((kappa + gran - 1) / gran) * gran, mfma_path(s.dtype) ? 256 : 64);
+      for (int b = 0; b < s.batch; b++)
+        CHECK(p.seq[b].split_keys <= kappa, "b %d: split of %d keys in a one-round plan of %lld",
+              b, p.seq[b].split_keys, (long long)kappa);
+    }
+  }
   *n_units_seen += p.n_units;
   const int nq = c.decode ? s.n_canvas : kCanvas;
   const int G = s.n_heads_q / s.n_heads_kv, Hkv = s.n_heads_kv;
@@ -155,10 +170,12 @@ static bool check_plan(const Case& c, long* n_units_seen) {
   const size_t bound = c.decode ? decode_workspace_bound(&s, Lmax, c.T, c.forced)
                                 : workspace_bound(&s, Lmax, c.T, c.forced);
   CHECK(ws <= bound, "workspace %zu above the bound %zu", ws, bound);
-  if (c.forced == 0)
-    CHECK((int64_t)p.n_units <= (int64_t)c.T + (int64_t)s.batch * Hkv * NRT,
-          "%d units above T + B*Hkv*NRT = %lld", p.n_units,
-          (long long)c.T + (long long)s.batch * Hkv * NRT);
+  if (c.forced == 0) {
+    const int64_t rounds = c.decode ? 1 : kMaxRounds;
+    CHECK((int64_t)p.n_units <= rounds * c.T + (int64_t)s.batch * Hkv * NRT,
+          "%d units above %lld*T + B*Hkv*NRT = %lld", p.n_units, (long long)rounds,
+          (long long)(rounds * c.T + (int64_t)s.batch * Hkv * NRT));
+  }
   return true;
 }
 
