@@ -191,10 +191,52 @@ def _stream(stream):
 
 
 def _prefix(prefix_len, batch):
-    arr = (ctypes.c_int32 * batch)(*[int(x) for x in prefix_len])
     if len(prefix_len) != batch:
         raise ValueError(f"prefix_len has {len(prefix_len)} entries, batch is {batch}")
-    return arr
+    return (ctypes.c_int32 * batch)(*[int(x) for x in prefix_len])
+
+
+def _check_like(items, device):
+    """Each (name, tensor, dtype, shape) must be a contiguous tensor of exactly that
+    type and shape on `device`: the kernels read and write these per position, with
+    only the sizes in the call's shape struct to go by."""
+    for name, t, dtype, shape in items:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a tensor")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+            raise ValueError(f"{name} is {tuple(t.shape)}, expected a contiguous {tuple(shape)}")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_sample(logits, noise_tokens, prev_argmax, out):
+    """Sampler call: noise_tokens, prev_argmax (optional) and the five outputs
+    (entropy, argmax, tokens, accepted, stop) against logits [B, n, V]."""
+    B, Nc, _ = logits.shape
+    if not isinstance(out, (tuple, list)) or len(out) != 5:
+        raise ValueError("out must hold five tensors: entropy, argmax, tokens, accepted, stop")
+    items = [("noise_tokens", noise_tokens, torch.int32, (B, Nc))]
+    if prev_argmax is not None:
+        items.append(("prev_argmax", prev_argmax, torch.int32, (B, Nc)))
+    names = ("entropy", "argmax", "tokens", "accepted", "stop")
+    types = (torch.float32, torch.int32, torch.int32, torch.int32, torch.int32)
+    shapes = ((B, Nc), (B, Nc), (B, Nc), (B, Nc), (B,))
+    items += list(zip(names, out, types, shapes))
+    _check_like(items, logits.device)
+
+
+def _check_selfcond(logits, embed, w1, w2, out):
+    """Self-conditioning call: E [V, d], W1 [d, h], W2 [h, d] and z [B, n, d]
+    against logits [B, n, V], all bf16 on the logits' device."""
+    B, nc, V = logits.shape
+    if not isinstance(w1, torch.Tensor) or w1.dim() != 2:
+        raise ValueError("w1 must be a 2-d tensor")
+    d, h = w1.shape
+    bf = torch.bfloat16
+    _check_like([("embed", embed, bf, (V, d)), ("w1", w1, bf, (d, h)), ("w2", w2, bf, (h, d)),
+                 ("out", out, bf, (B, nc, d))], logits.device)
 
 
 def workspace_bytes(batch, n_heads_q, n_heads_kv, head_dim, max_prefix_len,
@@ -365,13 +407,6 @@ def canvas_sample(logits, noise_tokens, prev_argmax=None, tau=0.8, budget=0.1,
     tensors."""
     _need(logits, "logits", torch.bfloat16, 3)
     B, Nc, V = logits.shape
-    _need(noise_tokens, "noise_tokens", torch.int32, 2)
-    if tuple(noise_tokens.shape) != (B, Nc):
-        raise ValueError("noise_tokens must be [B, 256]")
-    if prev_argmax is not None:
-        _need(prev_argmax, "prev_argmax", torch.int32, 2)
-        if tuple(prev_argmax.shape) != (B, Nc):
-            raise ValueError("prev_argmax must be [B, 256]")
     if out is None:
         dev = logits.device
         out = (torch.empty(B, Nc, dtype=torch.float32, device=dev),
@@ -379,6 +414,7 @@ def canvas_sample(logits, noise_tokens, prev_argmax=None, tau=0.8, budget=0.1,
                torch.empty(B, Nc, dtype=torch.int32, device=dev),
                torch.empty(B, Nc, dtype=torch.int32, device=dev),
                torch.empty(B, dtype=torch.int32, device=dev))
+    _check_sample(logits, noise_tokens, prev_argmax, out)
     entropy, argmax, tokens, accepted, stop = out
     shape = DgSampleShape(B, Nc, V, float(tau), float(budget), float(stop_entropy))
     st = lib.dg_canvas_sample(ctypes.byref(shape), _ptr(logits), _ptr(noise_tokens),
@@ -399,21 +435,17 @@ def self_condition(logits, embed, w1, w2, out=None, workspace=None, stream=None)
     """dg_self_condition: z = gelu(softmax(logits) E W1) W2 for bf16 logits
     [B, 256, V], E [V, d], W1 [d, h], W2 [h, d]; returns z [B, 256, d] bf16."""
     _need(logits, "logits", torch.bfloat16, 3)
-    _need(embed, "embed", torch.bfloat16, 2)
     _need(w1, "w1", torch.bfloat16, 2)
-    _need(w2, "w2", torch.bfloat16, 2)
     B, nc, V = logits.shape
     d, h = w1.shape
-    if embed.shape != (V, d) or w2.shape != (h, d):
-        raise ValueError(f"shapes: logits {tuple(logits.shape)}, embed {tuple(embed.shape)}, "
-                         f"w1 {tuple(w1.shape)}, w2 {tuple(w2.shape)}")
     if out is None:
         out = torch.empty((B, nc, d), dtype=torch.bfloat16, device=logits.device)
-    _need(out, "out", torch.bfloat16, 3)
+    _check_selfcond(logits, embed, w1, w2, out)
     shape = DgSelfcondShape(B, nc, V, d, h)
     if workspace is None:
         n = int(lib.dg_selfcond_workspace_bytes(ctypes.byref(shape)))
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=logits.device)
+    _check_workspace(workspace, logits.device)
     st = lib.dg_self_condition(ctypes.byref(shape), _ptr(logits), _ptr(embed), _ptr(w1), _ptr(w2),
                                _ptr(out), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream))

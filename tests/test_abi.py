@@ -345,3 +345,64 @@ def test_noalloc_rejects_before_any_hip_call(dg):
     st = dg.lib.dg_canvas_attn_noalloc(ctypes.byref(shape(dg)), None, ctypes.byref(cache), one,
                                        ctypes.byref(canvas), FAKE, None)
     assert st == -1
+
+
+def _sample_tensors(torch, B=2, n=256, V=64):
+    return dict(logits=torch.zeros(B, n, V, dtype=torch.bfloat16),
+                noise=torch.zeros(B, n, dtype=torch.int32),
+                prev=torch.zeros(B, n, dtype=torch.int32),
+                out=[torch.zeros(B, n, dtype=torch.float32)]
+                + [torch.zeros(B, n, dtype=torch.int32) for _ in range(3)]
+                + [torch.zeros(B, dtype=torch.int32)])
+
+
+def test_binding_sampler_checks(dg):
+    """The sampler writes entropy, argmax, tokens and accepted per position and stop
+    per canvas: caller-supplied outputs of another shape or type are refused."""
+    torch = pytest.importorskip("torch")
+    t = _sample_tensors(torch)
+    dg._check_sample(t["logits"], t["noise"], t["prev"], t["out"])
+    dg._check_sample(t["logits"], t["noise"], None, t["out"])
+    bad = [
+        ("noise", torch.zeros(2, 255, dtype=torch.int32), ValueError),
+        ("noise", torch.zeros(2, 256, dtype=torch.int64), TypeError),
+        ("prev", torch.zeros(1, 256, dtype=torch.int32), ValueError),
+        (0, torch.zeros(2, 256, dtype=torch.float16), TypeError),
+        (1, torch.zeros(2, 128, dtype=torch.int32), ValueError),
+        (4, torch.zeros(1, dtype=torch.int32), ValueError),
+        (2, torch.zeros(256, 2, dtype=torch.int32).t(), ValueError),  # not contiguous
+    ]
+    for key, val, exc in bad:
+        u = _sample_tensors(torch)
+        if isinstance(key, int):
+            u["out"][key] = val
+        else:
+            u[key] = val
+        with pytest.raises(exc):
+            dg._check_sample(u["logits"], u["noise"], u["prev"], u["out"])
+    with pytest.raises(ValueError, match="five"):
+        dg._check_sample(t["logits"], t["noise"], None, t["out"][:4])
+
+
+def test_binding_selfcond_checks(dg):
+    """z and the weights must agree with the logits' batch and vocabulary and with
+    each other's widths: a smaller z would be written past its end."""
+    torch = pytest.importorskip("torch")
+    bf = torch.bfloat16
+    B, V, d, h = 1, 64, 256, 128
+    lg = torch.zeros(B, 256, V, dtype=bf)
+    ok = dict(embed=torch.zeros(V, d, dtype=bf), w1=torch.zeros(d, h, dtype=bf),
+              w2=torch.zeros(h, d, dtype=bf), out=torch.zeros(B, 256, d, dtype=bf))
+    dg._check_selfcond(lg, **ok)
+    bad = [("embed", torch.zeros(V + 32, d, dtype=bf)), ("w2", torch.zeros(h, d + 256, dtype=bf)),
+           ("out", torch.zeros(B, 128, d, dtype=bf)), ("out", torch.zeros(B, 256, d, dtype=torch.float32))]
+    for key, val in bad:
+        kw = dict(ok)
+        kw[key] = val
+        with pytest.raises((ValueError, TypeError)):
+            dg._check_selfcond(lg, **kw)
+
+
+def test_binding_prefix_length_checked_first(dg):
+    with pytest.raises(ValueError, match="entries"):
+        dg._prefix([1, 2, 3], 2)
