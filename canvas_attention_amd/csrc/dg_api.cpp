@@ -405,6 +405,8 @@ dg_status dg_canvas_step_loop(const dg_shape* shape, int32_t n_steps, const void
                               const int32_t* prefix_len, void* out, int64_t out_step_stride,
                               void* workspace, size_t ws_bytes, void* stream) {
   if (n_steps < 0) return fail(DG_ERR_SHAPE, "n_steps %d is negative", n_steps);
+  if (q_step_stride < 0 || kv_step_stride < 0 || out_step_stride < 0)
+    return fail(DG_ERR_SHAPE, "step strides must be >= 0");
   Call c;
   dg_status st = prepare(shape, q, kv_cache, prefix_len, kv_canvas, out, workspace, ws_bytes,
                          kCanvasStep, &c);

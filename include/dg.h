@@ -44,7 +44,8 @@
  * Ownership: the caller owns every buffer (inputs, outputs, cache, workspace)
  * and keeps it alive until the work enqueued on `stream` has completed.  All
  * device pointers must be 16-byte aligned.  The library allocates no device
- * memory and keeps no state between calls.
+ * memory and keeps no state between calls, apart from the scratch array of
+ * dg_canvas_attn_noalloc and the record of the kernel timing hooks (both below).
  *
  * Streams and errors: `stream` is a hipStream_t passed as void* (NULL = the
  * default stream).  Every argument is validated on the host before any HIP
@@ -189,8 +190,8 @@ dg_status dg_commit_block(const dg_shape* shape, const void* q_blk, const dg_kv*
  * laid out as for dg_canvas_attn).  The result is bit for bit that of n_steps
  * separate dg_canvas_attn calls: in the model each step's queries depend on
  * the previous step's output, so steps are never fused; the loop plans once
- * and only removes per-call host work.  n_steps >= 0; the workspace is reused
- * by every step.
+ * and only removes per-call host work.  n_steps >= 0 and every stride >= 0
+ * (DG_ERR_SHAPE otherwise); the workspace is reused by every step.
  */
 dg_status dg_canvas_step_loop(const dg_shape* shape, int32_t n_steps, const void* q,
                               int64_t q_step_stride, const dg_kv* kv_canvas,

@@ -126,6 +126,11 @@ def test_step_loop_errors(dg):
     st = dg.lib.dg_canvas_step_loop(ctypes.byref(sh), 2, FAKE, 3, ctypes.byref(canv), 0,
                                     ctypes.byref(cache), pl, FAKE, 0, FAKE, 1 << 40, None)
     assert st == -7
+    for strides in ((-8, 0, 0), (0, -8, 0), (0, 0, -8)):
+        st = dg.lib.dg_canvas_step_loop(ctypes.byref(sh), 2, FAKE, strides[0], ctypes.byref(canv),
+                                        strides[1], ctypes.byref(cache), pl, FAKE, strides[2],
+                                        FAKE, 1 << 40, None)
+        assert st == -2 and b"stride" in dg.lib.dg_last_error()
 
 
 def test_fp8_step_strides(dg):
