@@ -13,8 +13,8 @@ steps of every cycle, so the step time holds attention and merge.  Beside it:
 canvas positions per second, the fraction of the bf16 MFMA peak, and the whole
 cycle's TFLOP/s (commit: 4*B*Hq*D*(256*L + 256*257/2)).  ms_per_step is the
 block cycle.  The roofline object is for the dominant kernel (the split-key
-canvas attention kernel), timed with HIP events that the library records on
-its launch stream.  cpu_baseline times the CPU fp64 oracle on bounded samples
+canvas attention kernel), timed with HIP events that the library's launches
+record with their own dispatch, on the launch stream.  cpu_baseline times the CPU fp64 oracle on bounded samples
 of the L=2048, L=8192 and L=131072 canvas steps, on all host threads and on
 one.  The default (bf16) line also carries the
 fp8 canvas step's kernel time and its fraction of the fp8 MFMA peak, the
@@ -435,7 +435,7 @@ def measure(dtype, steps, warmup, profile_steps=False):
     peak = PEAK_TFLOPS[dtype]
 
     # per-kernel durations: a second pass over the same canvas steps with the
-    # library's HIP events around every launch (same stream as the launches)
+    # library's HIP events, recorded by every launch with its dispatch
     dg.kernel_timing_read()
     dg.kernel_timing_enable(True)
     for _ in range(steps):

@@ -158,6 +158,31 @@ void time_end(int kind, hipStream_t st) {
   g_timing.count[kind] = k + 1;
 }
 
+// The event pair of the next timed launch of `kind`, recorded by the launch itself
+// with its dispatch (so the interval is the kernel's own execution, without the
+// time a separate event marker spends in the queue); null events when timing is
+// off or the record is full.  timing_commit keeps the pair once the launch has
+// been enqueued.
+dg::LaunchEvents timing_events(int kind) {
+  dg::LaunchEvents ev;
+  if (!g_timing.enabled) return ev;
+  const int k = g_timing.count[kind];
+  if (k >= kMaxTimed) return ev;
+  if (!g_timing.created[kind][k]) {
+    if (hipEventCreate(&g_timing.ev[kind][k][0]) != hipSuccess ||
+        hipEventCreate(&g_timing.ev[kind][k][1]) != hipSuccess)
+      return ev;
+    g_timing.created[kind][k] = true;
+  }
+  ev.start = g_timing.ev[kind][k][0];
+  ev.stop = g_timing.ev[kind][k][1];
+  return ev;
+}
+
+void timing_commit(int kind, const dg::LaunchEvents& ev) {
+  if (ev.start) g_timing.count[kind]++;
+}
+
 struct Call {
   dg_shape shape;
   Plan plan;
@@ -246,30 +271,30 @@ dg_status prepare(const dg_shape* shape, const void* q, const dg_kv* kv_cache,
 }
 
 dg_status launch(const Call& c, void* stream, bool timed = true) {
-  hipStream_t st = (hipStream_t)stream;
   const int dt = c.shape.dtype;
-  if (timed) time_begin(0, st);
+  const dg::LaunchEvents none;
+  dg::LaunchEvents ev = timed && c.plan.n_units > 0 ? timing_events(0) : none;
   int err;
   if (c.mode == kDecode && mfma_path(dt))
-    err = dg::launch_decode(c.args, c.plan, dt, c.shape.head_dim, stream);
+    err = dg::launch_decode(c.args, c.plan, dt, c.shape.head_dim, stream, ev);
   else if (dt == DG_BF16)
-    err = dg::launch_attn_bf16(c.args, c.plan, c.shape.head_dim, c.causal, stream);
+    err = dg::launch_attn_bf16(c.args, c.plan, c.shape.head_dim, c.causal, stream, ev);
   else if (dt == DG_FP8)
-    err = dg::launch_attn_fp8(c.args, c.plan, c.causal, stream);
+    err = dg::launch_attn_fp8(c.args, c.plan, c.causal, stream, ev);
   else
-    err = dg::launch_attn_f32(c.args, c.plan, c.shape.head_dim, c.causal, stream);
-  if (timed) time_end(0, st);
+    err = dg::launch_attn_f32(c.args, c.plan, c.shape.head_dim, c.causal, stream, ev);
   if (err != 0)
     return fail(DG_ERR_HIP, "attention kernel launch failed: %s",
                 hipGetErrorString((hipError_t)err));
+  timing_commit(0, ev);
   bool any = false;
   for (int b = 0; b < c.plan.batch; b++) any = any || c.plan.seq[b].n_splits > 1;
   if (any) {
-    if (timed) time_begin(1, st);
-    err = dg::launch_merge(c.args, c.plan, c.shape.head_dim, dt != DG_F32, stream);
-    if (timed) time_end(1, st);
+    ev = timed ? timing_events(1) : none;
+    err = dg::launch_merge(c.args, c.plan, c.shape.head_dim, dt != DG_F32, stream, ev);
     if (err != 0)
       return fail(DG_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString((hipError_t)err));
+    timing_commit(1, ev);
   }
   if (getenv("DG_LOG")) {
     static const char* const kModeName[] = {"canvas", "commit", "decode"};

@@ -157,19 +157,21 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, Plan plan) {
 
 }  // namespace
 
-int launch_attn_f32(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream) {
+int launch_attn_f32(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream,
+                    const LaunchEvents& ev) {
   hipStream_t st = (hipStream_t)stream;
   if (p.n_units == 0) return 0;
+  const dim3 grid(p.n_units), block(64);
   if (head_dim == 128) {
     if (causal)
-      hipLaunchKernelGGL((attn_f32_kernel<128, true>), dim3(p.n_units), dim3(64), 0, st, a, p);
+      hipExtLaunchKernelGGL((attn_f32_kernel<128, true>), grid, block, 0, st, ev.start, ev.stop, 0, a, p);
     else
-      hipLaunchKernelGGL((attn_f32_kernel<128, false>), dim3(p.n_units), dim3(64), 0, st, a, p);
+      hipExtLaunchKernelGGL((attn_f32_kernel<128, false>), grid, block, 0, st, ev.start, ev.stop, 0, a, p);
   } else {
     if (causal)
-      hipLaunchKernelGGL((attn_f32_kernel<64, true>), dim3(p.n_units), dim3(64), 0, st, a, p);
+      hipExtLaunchKernelGGL((attn_f32_kernel<64, true>), grid, block, 0, st, ev.start, ev.stop, 0, a, p);
     else
-      hipLaunchKernelGGL((attn_f32_kernel<64, false>), dim3(p.n_units), dim3(64), 0, st, a, p);
+      hipExtLaunchKernelGGL((attn_f32_kernel<64, false>), grid, block, 0, st, ev.start, ev.stop, 0, a, p);
   }
   return (int)hipGetLastError();
 }

@@ -1487,49 +1487,56 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(AttnArgs a, Plan plan) 
 }
 
 template <class F, int D, int NST>
-int launch_decode_t(const AttnArgs& a, const Plan& p, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<F, D, kDecodeWaves, NST>), dim3(p.n_units), dim3(64 * kDecodeWaves),
-                     0, st, a, p);
+int launch_decode_t(const AttnArgs& a, const Plan& p, hipStream_t st, const LaunchEvents& ev) {
+  hipExtLaunchKernelGGL((decode_kernel<F, D, kDecodeWaves, NST>), dim3(p.n_units),
+                        dim3(64 * kDecodeWaves), 0, st, ev.start, ev.stop, 0, a, p);
   return (int)hipGetLastError();
 }
 
 template <int D, bool CAUSAL, int WM, int WK, int NSLOT>
-int launch_one(const AttnArgs& a, const Plan& p, hipStream_t st) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, WM, WK, NSLOT>), dim3(p.n_units), dim3(512), 0,
-                     st, a, p);
+int launch_one(const AttnArgs& a, const Plan& p, hipStream_t st, const LaunchEvents& ev) {
+  hipExtLaunchKernelGGL((attn_bf16_kernel<D, CAUSAL, WM, WK, NSLOT>), dim3(p.n_units), dim3(512), 0,
+                        st, ev.start, ev.stop, 0, a, p);
   return (int)hipGetLastError();
 }
 
 
 template <bool CAUSAL>
-int launch_fp8(const AttnArgs& a, const Plan& p, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fp8_kernel<128, CAUSAL, 4, 2, 4>), dim3(p.n_units), dim3(512), 0, st, a, p);
+int launch_fp8(const AttnArgs& a, const Plan& p, hipStream_t st, const LaunchEvents& ev) {
+  hipExtLaunchKernelGGL((attn_fp8_kernel<128, CAUSAL, 4, 2, 4>), dim3(p.n_units), dim3(512), 0, st,
+                        ev.start, ev.stop, 0, a, p);
   return (int)hipGetLastError();
 }
 
 }  // namespace
 
-int launch_attn_fp8(const AttnArgs& a, const Plan& p, bool causal, void* stream) {
+int launch_attn_fp8(const AttnArgs& a, const Plan& p, bool causal, void* stream,
+                    const LaunchEvents& ev) {
+  hipStream_t st = (hipStream_t)stream;
   if (p.n_units == 0) return 0;
-  return causal ? launch_fp8<true>(a, p, (hipStream_t)stream) : launch_fp8<false>(a, p, (hipStream_t)stream);
+  return causal ? launch_fp8<true>(a, p, st, ev) : launch_fp8<false>(a, p, st, ev);
 }
 
-int launch_decode(const AttnArgs& a, const Plan& p, int dtype, int head_dim, void* stream) {
+int launch_decode(const AttnArgs& a, const Plan& p, int dtype, int head_dim, void* stream,
+                  const LaunchEvents& ev) {
   hipStream_t st = (hipStream_t)stream;
   if (p.n_units == 0) return 0;
   // two stages of 16 KB (K and V chunk) per wave at head_dim 128, four of 8 KB at 64
-  if (dtype == DG_FP8) return launch_decode_t<FmtFp8, 128, 2>(a, p, st);
-  if (head_dim == 128) return launch_decode_t<FmtBf16, 128, 2>(a, p, st);
-  return launch_decode_t<FmtBf16, 64, 4>(a, p, st);
+  if (dtype == DG_FP8) return launch_decode_t<FmtFp8, 128, 2>(a, p, st, ev);
+  if (head_dim == 128) return launch_decode_t<FmtBf16, 128, 2>(a, p, st, ev);
+  return launch_decode_t<FmtBf16, 64, 4>(a, p, st, ev);
 }
 
-int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream) {
+int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream,
+                     const LaunchEvents& ev) {
   hipStream_t st = (hipStream_t)stream;
   if (p.n_units == 0) return 0;
   // 128 packed rows per unit: four row groups x two key groups
   if (head_dim == 128)
-    return causal ? launch_one<128, true, 4, 2, 4>(a, p, st) : launch_one<128, false, 4, 2, 4>(a, p, st);
-  return causal ? launch_one<64, true, 4, 2, 8>(a, p, st) : launch_one<64, false, 4, 2, 8>(a, p, st);
+    return causal ? launch_one<128, true, 4, 2, 4>(a, p, st, ev)
+                  : launch_one<128, false, 4, 2, 4>(a, p, st, ev);
+  return causal ? launch_one<64, true, 4, 2, 8>(a, p, st, ev)
+                : launch_one<64, false, 4, 2, 8>(a, p, st, ev);
 }
 
 }  // namespace dg

@@ -2,6 +2,7 @@
 // (the split-key plan and its unit decode are in dg_plan.h).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "dg.h"
@@ -68,14 +69,26 @@ struct SelfcondArgs {
   void (*time_end)(int kind, hipStream_t st);
 };
 
+// Events that a launch records with its own dispatch (hipExtLaunchKernelGGL), so
+// that the time between them is the kernel's execution alone; the library's
+// kernel timing hooks pass them.  Both null: a plain launch.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // Host-side launchers (defined next to their kernels).  Each returns the HIP
 // error of the launch.
-int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream);
-int launch_attn_fp8(const AttnArgs& a, const Plan& p, bool causal, void* stream);
-int launch_attn_f32(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream);
-int launch_merge(const AttnArgs& a, const Plan& p, int head_dim, bool bf16_out, void* stream);
+int launch_attn_bf16(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream,
+                     const LaunchEvents& ev);
+int launch_attn_fp8(const AttnArgs& a, const Plan& p, bool causal, void* stream,
+                    const LaunchEvents& ev);
+int launch_attn_f32(const AttnArgs& a, const Plan& p, int head_dim, bool causal, void* stream,
+                    const LaunchEvents& ev);
+int launch_merge(const AttnArgs& a, const Plan& p, int head_dim, bool bf16_out, void* stream,
+                 const LaunchEvents& ev);
 int launch_sample(const SampleArgs& s, void* stream);
-int launch_decode(const AttnArgs& a, const Plan& p, int dtype, int head_dim, void* stream);
+int launch_decode(const AttnArgs& a, const Plan& p, int dtype, int head_dim, void* stream,
+                  const LaunchEvents& ev);
 int launch_selfcond(const SelfcondArgs& a, void* stream);
 // contraction rows per split of a self-conditioning product (a multiple of 32)
 int selfcond_splits(int K, int N, int M, int cus);

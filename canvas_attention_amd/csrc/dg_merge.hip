@@ -201,27 +201,32 @@ __global__ __launch_bounds__(256) void merge_dec_kernel(AttnArgs a, Plan plan) {
 }
 
 template <int D, bool BF16OUT>
-int launch_t(const AttnArgs& a, const Plan& p, hipStream_t st) {
+int launch_t(const AttnArgs& a, const Plan& p, hipStream_t st, const LaunchEvents& ev) {
   constexpr int RPB = 256 / (D / (BF16OUT ? 8 : 4));
   const int rows = a.n_heads_q * p.n_q;  // per sequence
   const dim3 grid((rows + RPB - 1) / RPB, p.batch);
   if (p.n_q != kCanvas && BF16OUT && p.rows_per_unit == 32) {  // matrix-core decode
     const int chunks = rows * (D / 8);
-    hipLaunchKernelGGL((merge_dec_kernel<D>), dim3((chunks + 31) / 32, p.batch), dim3(256), 0, st, a, p);
-  } else if (p.n_q == kCanvas)
-    hipLaunchKernelGGL((merge_kernel<D, BF16OUT, false>), grid, dim3(256), 0, st, a, p);
-  else
-    hipLaunchKernelGGL((merge_kernel<D, BF16OUT, true>), grid, dim3(256), 0, st, a, p);
+    hipExtLaunchKernelGGL((merge_dec_kernel<D>), dim3((chunks + 31) / 32, p.batch), dim3(256), 0, st,
+                          ev.start, ev.stop, 0, a, p);
+  } else if (p.n_q == kCanvas) {
+    hipExtLaunchKernelGGL((merge_kernel<D, BF16OUT, false>), grid, dim3(256), 0, st, ev.start, ev.stop,
+                          0, a, p);
+  } else {
+    hipExtLaunchKernelGGL((merge_kernel<D, BF16OUT, true>), grid, dim3(256), 0, st, ev.start, ev.stop,
+                          0, a, p);
+  }
   return (int)hipGetLastError();
 }
 
 }  // namespace
 
-int launch_merge(const AttnArgs& a, const Plan& p, int head_dim, bool bf16_out, void* stream) {
+int launch_merge(const AttnArgs& a, const Plan& p, int head_dim, bool bf16_out, void* stream,
+                 const LaunchEvents& ev) {
   hipStream_t st = (hipStream_t)stream;
   if (head_dim == 128)
-    return bf16_out ? launch_t<128, true>(a, p, st) : launch_t<128, false>(a, p, st);
-  return bf16_out ? launch_t<64, true>(a, p, st) : launch_t<64, false>(a, p, st);
+    return bf16_out ? launch_t<128, true>(a, p, st, ev) : launch_t<128, false>(a, p, st, ev);
+  return bf16_out ? launch_t<64, true>(a, p, st, ev) : launch_t<64, false>(a, p, st, ev);
 }
 
 }  // namespace dg
