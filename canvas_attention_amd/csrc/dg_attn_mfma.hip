@@ -46,7 +46,8 @@
 //   * Softmax runs in the log2 domain with a lazily raised reference max: a
 //     chunk's exact max is always formed, but the output is rescaled only when it
 //     exceeds the reference by more than 64 (so every exponential stays <= 2^64);
-//     in steady state a score costs max, FMA, exp2, a bf16 pack and a dot2 sum.
+//     in steady state a score costs max, FMA, exp2, a bf16 pack and an fp32 add
+//     (fp8: the row sum comes from one more MFMA per chunk instead).
 //     The result is exact attention; only the point at which the max is folded
 //     in moves.
 //   * Key groups of a workgroup are merged through LDS at the end; the unit
