@@ -10,7 +10,7 @@
 //
 // Two launches:
 //   * row_stats_kernel: one workgroup per position streams its logits once
-//     (bf16, 16-byte loads, eight in flight per lane) and forms the entropy of
+//     (bf16, 16-byte loads, four in flight per lane) and forms the entropy of
 //     softmax(logits / tau) and the argmax.  HBM-bound: 512 KB per position at a
 //     262144-token vocabulary.
 //   * select_kernel: one workgroup per canvas: budgeted acceptance, tokens and
@@ -23,8 +23,13 @@
 namespace dg {
 namespace {
 
+// Bytes in flight: kBatch 16-byte loads per lane and batch, two batches in
+// flight, 512 lanes: 32 KB per CU, 8 MB over the chip, about what HBM's
+// bandwidth-delay product asks for.  Deeper batches (64 KB or 128 KB per CU, or
+// more waves) queue more requests behind each row's stream and measured slower:
+// 32.3 us per call at kBatch = 8, 27.9-28.4 us at kBatch = 2.
 constexpr int kStatThreads = 512;
-constexpr int kBatch = 8;           // 16-byte loads per lane per batch (64 logits)
+constexpr int kBatch = 2;           // 16-byte loads per lane per batch (16 logits)
 constexpr float kRefSlack = 16.f;   // log2 units an exponential may exceed 1 by
 
 // Running statistics of a slice of a row.  The exponentials are taken in the
@@ -42,12 +47,15 @@ struct RowAcc {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// max of 64 values as one v_max3 chain (logits are finite or -inf: no NaN handling)
-__device__ __forceinline__ float max64(const float (&x)[64]) {
+// max of N (even) values as one v_max3 chain (logits are finite or -inf: no NaN
+// handling)
+template <int N>
+__device__ __forceinline__ float max_of(const float (&x)[N]) {
+  static_assert(N % 2 == 0 && N >= 2, "an even count");
   float m = x[0];
 #pragma unroll
-  for (int i = 1; i < 63; i += 2) asm("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(m), "v"(x[i]), "v"(x[i + 1]));
-  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(m), "v"(x[63]));
+  for (int i = 1; i < N - 1; i += 2) asm("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(m), "v"(x[i]), "v"(x[i + 1]));
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(m), "v"(x[N - 1]));
   return m;
 }
 
@@ -62,9 +70,9 @@ __device__ __forceinline__ void merge_sums(float& r, float& z, float& s, float r
 }
 
 // logits [rows][V] bf16, V a multiple of 8; entropy and argmax [rows].  Lane t's
-// batch k holds the 16-byte chunks (k * kBatch + e) * 512 + t, e = 0..7: every load
-// instruction of a wave reads 1 KB of consecutive logits, and a lane's batches
-// come in increasing index order.  -inf logits (masked tokens) are allowed; a
+// batch k holds the 16-byte chunks (k * kBatch + e) * 512 + t, e = 0..kBatch-1:
+// every load instruction of a wave reads 1 KB of consecutive logits, and a lane's
+// batches come in increasing index order.  -inf logits (masked tokens) are allowed; a
 // row needs one finite logit.
 __global__ __launch_bounds__(kStatThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void row_stats_kernel(const uint16_t* logits, int vocab,
                                                                  float c, float* entropy,
@@ -76,9 +84,9 @@ __global__ __launch_bounds__(kStatThreads) __attribute__((amdgpu_waves_per_eu(2,
   const int nbatches = (nchunks + kBatch * kStatThreads - 1) / (kBatch * kStatThreads);
   RowAcc a{-INFINITY, 0, -1e30f, 0.f, 0.f};
 
-  // One batch: 64 logits per lane, reduced into the lane's statistics.
+  // One batch: 8 * kBatch logits per lane, reduced into the lane's statistics.
   auto reduce_batch = [&](const uint4 (&v)[kBatch], int k) {
-    float x[64];
+    float x[8 * kBatch];
 #pragma unroll
     for (int e = 0; e < kBatch; e++) {
       const uint32_t w[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(kStatThreads) __attribute__((amdgpu_waves_per_eu(2,
         x[8 * e + 2 * q + 1] = bf16_hi(w[q]);
       }
     }
-    const float cm = max64(x);
+    const float cm = max_of(x);
     if (cm > a.best) {  // strict: a lane keeps the first batch that reached its max
       a.best = cm;
       a.bk = k;
@@ -103,7 +111,7 @@ __global__ __launch_bounds__(kStatThreads) __attribute__((amdgpu_waves_per_eu(2,
     }
     float z = 0.f, s = 0.f;
 #pragma unroll
-    for (int j = 0; j < 64; j++) {
+    for (int j = 0; j < 8 * kBatch; j++) {
       // clamped so that a -inf logit (masked token) gives p = 0 and p * y = 0
       // (2^-200 is 0 in fp32); the kernel is bound by HBM, not by this max
       const float y = __builtin_fmaxf(__builtin_fmaf(x[j], c, -a.r), -200.f);
