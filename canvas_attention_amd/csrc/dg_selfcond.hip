@@ -8,9 +8,9 @@
 //
 // Three kernels, seven launches per call:
 //   * softmax_blocks_kernel: one wave per row and vocabulary split (8192
-//     entries).  The split's logits stay in registers: the wave takes the max,
-//     writes exp(x - max) rounded to bf16, and the split's (max, sum of the
-//     rounded weights).  The weights go out in the blocked layout the product
+//     entries), four waves per block and one block per CU.  The split's logits
+//     stay in registers: the wave takes the max, writes exp(x - max) rounded to
+//     bf16, and the split's (max, sum of the rounded weights).  The weights go out in the blocked layout the product
 //     kernel reads, [V/32][M][32] -- the 32 entries of a block of every row
 //     consecutive -- so a stage of that kernel is one contiguous 16 KB tile; the
 //     waves of adjacent rows in one block fill whole 128-byte lines.
@@ -97,6 +97,12 @@ __global__ __launch_bounds__(64 * NW) void softmax_blocks_kernel(SelfcondArgs a)
   const int v0 = s * kSelfcondSplit;
   const int nch = min(kSelfcondSplit, V - v0) / 8;  // valid chunks of the segment
   const float L2E = 1.4426950408889634f;
+  // Reserved so that one block runs per CU.  Each wave requests its whole 16 KB
+  // segment at once; four waves per CU keep 64 KB in flight (16 MB over the chip),
+  // while the 8-wave blocks this replaces kept 128 KB and ran 10% slower: requests
+  // beyond what keeps HBM busy only queue.  The store never runs (V >= 32).
+  __shared__ char occupancy_pad[96 * 1024];
+  if (V < 0) occupancy_pad[threadIdx.x] = 1;
   uint4 x[RPW][CPL];
 #pragma unroll
   for (int rr = 0; rr < RPW; rr++) {
@@ -426,9 +432,9 @@ int launch_selfcond(const SelfcondArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int M = a.rows;
   if (a.time_begin) a.time_begin(1, st);
-  // one row per wave (168 VGPRs, three waves per SIMD) measured 10% faster than two
-  // rows per wave (240 VGPRs, two per SIMD)
-  hipLaunchKernelGGL((softmax_blocks_kernel<8, 1>), dim3(a.vocab_splits, M / 8), dim3(512), 0, st, a);
+  // one row per wave measured 10% faster than two rows per wave (240 VGPRs), and
+  // blocks of four waves held to one per CU 10% faster than blocks of eight
+  hipLaunchKernelGGL((softmax_blocks_kernel<4, 1>), dim3(a.vocab_splits, M / 4), dim3(256), 0, st, a);
   if (a.time_end) a.time_end(1, st);
   int err = (int)hipGetLastError();
   if (err) return err;
